@@ -1,0 +1,199 @@
+/*
+ * pkvg.h -- paged MLA KV-cache gather for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpkvg.so.  The gather copies each request's cached context,
+ * scattered over physical pages of a paged KV cache and addressed through an
+ * int32 block table, into one contiguous destination of num_tokens rows, as
+ * chunked prefill needs it.  Method: the prhub.com.cn summary of vLLM pull
+ * request 51739, "MLA cache gather scheduled by logical page; raw copy up to
+ * 331x faster" -- its sections "implementation breakdown" (step 1: one
+ * workgroup per logical page, partial first/last pages, vector and scalar
+ * stride paths; step 2: the destination is sliced to exactly num_tokens rows)
+ * and "key source snippets" (the page-task fields and the per-token
+ * reference the kernels must match).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every array pointer is a DEVICE pointer on the calling thread's current
+ *    HIP device.  The caller owns all memory; the library keeps no pointer
+ *    after a call returns.
+ *  - Strides are in ELEMENTS of their own array (like torch.Tensor.stride());
+ *    the innermost stride of the cache and of the destination is 1.
+ *  - The cache is [num_blocks, block_size, >= entry] with strides
+ *    (src_block_stride, src_token_stride, 1); the first `entry` elements of
+ *    each cache row are gathered.
+ *  - The destination is [num_tokens, >= entry] with strides
+ *    (dst_row_stride, 1); only columns [0, entry) of rows in [0, num_tokens)
+ *    may be written.
+ *  - block_table is int32 [num_reqs, >= block_table_width] with row pitch
+ *    block_table_ld; entry [r][l] is the physical block holding logical page
+ *    l of request r.
+ *  - cu_seq_lens is int32 [num_reqs + 1]: request r writes output rows
+ *    [min(cu[r], T), min(cu[r+1], T)) with T = num_tokens (the clamps of the
+ *    page-task map).  seq_starts is int32 [num_reqs] or NULL: request r reads
+ *    its context from token seq_starts[r] on (0 when NULL); output row
+ *    min(cu[r],T) + i takes token t = seq_starts[r] + i, i.e. slot
+ *    t % block_size of physical block block_table[r][t / block_size].
+ *  - Guards: a page whose logical block is >= block_table_width, or whose
+ *    physical id lies outside [0, num_blocks), is skipped and its output rows
+ *    are left untouched (the bound check the page's review section asks for).
+ *    Bad device-side data is therefore not an error and is never reported.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream) and is asynchronous: nothing synchronises with the host.  The
+ *    caller keeps every buffer alive until the stream has passed the work.
+ *  - Calls are thread-safe and re-entrant.  Requests with more than
+ *    PKVG_FUSED_MAX_REQS entries allocate a stream-ordered scratch buffer
+ *    (hipMallocAsync / hipFreeAsync on `stream`); smaller ones allocate nothing.
+ *  - Preconditions (not checked, out of contract): cu_seq_lens is
+ *    non-decreasing with cu[0] >= 0; seq_starts >= 0; the source and
+ *    destination do not overlap.
+ *  - Return value: PKVG_OK (0) on success.  Argument errors return a nonzero
+ *    PKVG_E_* code BEFORE anything is enqueued.  num_reqs == 0 or
+ *    num_tokens == 0 returns PKVG_OK without enqueueing anything.
+ */
+#ifndef PKVG_H
+#define PKVG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PKVG_OK 0
+#define PKVG_E_NULL 1   /* a required pointer is NULL while there is work to do */
+#define PKVG_E_SHAPE 2  /* a count or size is out of range (negative, zero where positive is required) */
+#define PKVG_E_STRIDE 3 /* a stride is negative, or the destination rows overlap (dst_row_stride < entry),
+                           or block_table_ld < block_table_width */
+#define PKVG_E_DTYPE 4  /* unsupported element size or kv_cache_dtype */
+#define PKVG_E_LIMIT 5  /* beyond an implementation limit: block_size * row bytes >= 2^31, or
+                           num_tokens / block_size + 2 * num_reqs >= 2^31 */
+#define PKVG_E_HIP 6    /* a HIP runtime call failed (launch or allocation); see pkvg_last_hip_error */
+
+/* kv_cache_dtype values for gather_maybe_dequant */
+#define PKVG_KV_AUTO 0     /* cache holds bf16 entries: bit copy into the bf16 destination */
+#define PKVG_KV_FP8_E4M3 1 /* cache holds OCP e4m3fn codes: dequantise into the bf16 destination */
+
+/* requests up to this count build their page tasks inside the gather kernel
+ * (no scratch); larger batches use a separate builder and a scratch buffer */
+#define PKVG_FUSED_MAX_REQS 1024
+
+/* one page task as written by gather_page_tasks: 8 int32 (32 bytes) */
+#define PKVG_TASK_INTS 8
+
+/*
+ * gather_cache -- raw copy gather (the page's cp_gather_cache).
+ *
+ * Copies `entry` elements of `elem_bytes` bytes each (1, 2, 4 or 8) from the
+ * cache rows described above into the destination rows, bit for bit.
+ *
+ *   src_cache         device, [num_blocks, block_size, >=entry] elements of elem_bytes
+ *   elem_bytes        1, 2, 4 or 8 (the same for source and destination)
+ *   num_blocks        >= 0: physical blocks in the cache (the guard bound)
+ *   block_size        > 0: tokens per page
+ *   entry             > 0: elements gathered per token
+ *   src_block_stride  >= 0, src_token_stride >= 0: cache strides, in elements
+ *   dst               device, [num_tokens, >=entry]; dst_row_stride >= entry
+ *   num_tokens        >= 0: T, rows of dst
+ *   block_table       device int32; block_table_width >= 0; block_table_ld >= width
+ *   cu_seq_lens       device int32 [num_reqs + 1]
+ *   seq_starts        device int32 [num_reqs] or NULL
+ *   num_reqs          >= 0
+ *   stream            hipStream_t or NULL
+ *
+ * Errors: PKVG_E_NULL (src_cache, dst, block_table or cu_seq_lens NULL with
+ * work to do), PKVG_E_SHAPE, PKVG_E_STRIDE, PKVG_E_DTYPE (elem_bytes),
+ * PKVG_E_LIMIT, PKVG_E_HIP.
+ */
+int gather_cache(const void *src_cache, int32_t elem_bytes,
+                 int64_t num_blocks, int32_t block_size, int32_t entry,
+                 int64_t src_block_stride, int64_t src_token_stride,
+                 void *dst, int64_t num_tokens, int64_t dst_row_stride,
+                 const int32_t *block_table, int32_t block_table_width,
+                 int64_t block_table_ld,
+                 const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                 int32_t num_reqs, void *stream);
+
+/*
+ * gather_maybe_dequant -- gather into a bf16 destination, dequantising when
+ * the cache is fp8 (the page's gather_and_maybe_dequant_cache).
+ *
+ *   kv_cache_dtype == PKVG_KV_AUTO: the cache holds bf16 elements (strides in
+ *     bf16 elements); each element is copied bit for bit; `scale` is ignored
+ *     and may be NULL.
+ *   kv_cache_dtype == PKVG_KV_FP8_E4M3: the cache holds one-byte OCP e4m3fn
+ *     codes (strides in bytes); each element becomes
+ *     bf16_rne(fp32(decode(code)) * scale[0]), one fp32 multiply rounded to
+ *     nearest-even, then rounded to bf16 nearest-even.  `scale` is a device
+ *     pointer to one fp32 (per-tensor scale), read on the device.
+ *
+ * dst is bf16 (2-byte elements) with row stride dst_row_stride elements.  The
+ * other arguments are as for gather_cache.  Errors: as gather_cache, plus
+ * PKVG_E_DTYPE for an unknown kv_cache_dtype and PKVG_E_NULL for a NULL scale
+ * with PKVG_KV_FP8_E4M3.
+ */
+int gather_maybe_dequant(const void *src_cache, int32_t kv_cache_dtype,
+                         int64_t num_blocks, int32_t block_size, int32_t entry,
+                         int64_t src_block_stride, int64_t src_token_stride,
+                         void *dst, int64_t num_tokens, int64_t dst_row_stride,
+                         const int32_t *block_table, int32_t block_table_width,
+                         int64_t block_table_ld,
+                         const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                         int32_t num_reqs, const float *scale, void *stream);
+
+/*
+ * gather_upconvert_fp8 -- fp8 (OCP e4m3fn) cache to bf16 destination (the
+ * page's cp_gather_and_upconvert_fp8_kv_cache, with coalesced bf16 writes).
+ * Same arithmetic as gather_maybe_dequant with PKVG_KV_FP8_E4M3; `scale`
+ * (device, one fp32) is required.  Cache strides are in bytes, destination
+ * strides in bf16 elements.
+ */
+int gather_upconvert_fp8(const void *src_cache,
+                         int64_t num_blocks, int32_t block_size, int32_t entry,
+                         int64_t src_block_stride, int64_t src_token_stride,
+                         void *dst, int64_t num_tokens, int64_t dst_row_stride,
+                         const int32_t *block_table, int32_t block_table_width,
+                         int64_t block_table_ld,
+                         const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                         int32_t num_reqs, const float *scale, void *stream);
+
+/*
+ * gather_page_tasks -- the page-task builder on its own (the page's
+ * GatherPageTask / map_gather_page_task, built as an exclusive scan of
+ * per-request page counts plus a binary search instead of a linear scan).
+ *
+ * Writes, for task k < min(count, capacity), PKVG_TASK_INTS int32 at
+ * tasks[k * PKVG_TASK_INTS]: req_id, logical_block, page_token_begin,
+ * page_token_end (exclusive), output_token_begin, physical_block (-1 when the
+ * guards skip the page), 0, 0; and writes count to num_tasks[0] (device).
+ * Tasks are ordered by request, then logical page.  A request that gathers no
+ * rows contributes no task.
+ *
+ *   cu_seq_lens, seq_starts, num_reqs, num_tokens, block_size: as above
+ *   block_table, block_table_width, block_table_ld, num_blocks: as above
+ *   tasks      device int32 [capacity * PKVG_TASK_INTS]
+ *   capacity   >= 0 task records available
+ *   num_tasks  device int32 [1]
+ *
+ * Errors: PKVG_E_NULL, PKVG_E_SHAPE, PKVG_E_STRIDE, PKVG_E_LIMIT, PKVG_E_HIP.
+ * num_reqs == 0 still writes num_tasks[0] = 0.
+ */
+int gather_page_tasks(const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                      int32_t num_reqs, int64_t num_tokens, int32_t block_size,
+                      const int32_t *block_table, int32_t block_table_width,
+                      int64_t block_table_ld, int64_t num_blocks,
+                      int32_t *tasks, int64_t capacity, int32_t *num_tasks,
+                      void *stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *pkvg_status_string(int status);
+
+/* The hipError_t of the calling thread's last PKVG_E_HIP, or 0. */
+int pkvg_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKVG_H */

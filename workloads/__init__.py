@@ -1,0 +1,283 @@
+"""Seeded synthetic inputs for the paged MLA KV-cache gather.
+
+This module is shared by the tests, the smoke check and the benchmark, and by
+both sides of every parity check (the HIP library and the CPU oracle).  It
+holds none of the gather's arithmetic: it only draws caches, block tables,
+per-request lengths and starts, and allocates sentinel-filled destinations.
+
+Recipe (all draws from one ``torch.Generator('cpu')`` seeded per workload, in
+this order: request lengths, seq_starts, physical block permutation, cache
+values):
+
+* bf16 caches: ``randn`` in fp32, rounded to bf16 (N(0,1) values).
+* fp8 caches: uniform over the 254 non-NaN e4m3fn codes (0x7F and 0xFF are
+  the two NaN codes and are never drawn).
+* block tables: one ``randperm(num_blocks)`` dealt out request after request,
+  ``ceil(context_len / block_size)`` distinct physical blocks per request; the
+  unused tail of each row is -1, so a stray read of an unused slot shows up as
+  rows left untouched.
+* ``cu_seq_lens`` are prefix sums (R + 1 entries, starting at 0) of the rows
+  gathered per request; with ``seq_starts`` a request gathers the context
+  tokens ``[start, context_len)``.
+* destinations are filled with a sentinel byte pattern (0xFF) so rows the
+  gather must not touch can be checked.
+
+The five named workloads follow the shapes the pages' scenarios and tests use
+(single-request 60K and 300K contexts, a skewed batch with seq_starts, a tiny
+uneven batch, a mixed batch with non-vector strides).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+SENTINEL_BYTE = 0xFF
+
+# kind of gather a workload exercises
+RAW = "raw"                # gather_cache: bit copy
+DEQUANT_AUTO = "dequant_auto"  # gather_maybe_dequant with kv_cache_dtype 'auto' (bit copy of bf16)
+DEQUANT_FP8 = "dequant_fp8"    # gather_maybe_dequant with kv_cache_dtype 'fp8'
+UPCONVERT = "upconvert"    # gather_upconvert_fp8
+
+FP8_KINDS = (DEQUANT_FP8, UPCONVERT)
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    kind: str
+    block_size: int
+    entry: int                      # elements per cache row that are gathered
+    cache_base: torch.Tensor        # [num_blocks, block_size, cache_cols] (bf16 or uint8)
+    workspace: torch.Tensor         # [workspace_rows, dst_cols] (dst dtype), sentinel filled
+    num_tokens: int                 # T: rows of dst = workspace[:T, :entry]
+    block_table: torch.Tensor       # int32 [R, W]
+    cu_seq_lens: torch.Tensor       # int32 [R + 1]
+    seq_starts: Optional[torch.Tensor]  # int32 [R] or None
+    context_lens: list
+    scale: float = 1.0
+    scale_tensor: Optional[torch.Tensor] = None  # fp32 [1] for fp8 kinds
+
+    @property
+    def num_reqs(self) -> int:
+        return self.block_table.shape[0]
+
+    @property
+    def num_blocks(self) -> int:
+        return self.cache_base.shape[0]
+
+    def src_cache(self) -> torch.Tensor:
+        return self.cache_base[..., : self.entry]
+
+    def dst(self) -> torch.Tensor:
+        return self.workspace[: self.num_tokens, : self.entry]
+
+    def to(self, device) -> "Workload":
+        """A copy whose tensors live on ``device`` (strides of the views are kept)."""
+        d = dataclasses.replace(self)
+        d.cache_base = self.cache_base.to(device)
+        d.workspace = self.workspace.to(device)
+        d.block_table = self.block_table.to(device)
+        d.cu_seq_lens = self.cu_seq_lens.to(device)
+        d.seq_starts = None if self.seq_starts is None else self.seq_starts.to(device)
+        d.scale_tensor = None if self.scale_tensor is None else self.scale_tensor.to(device)
+        return d
+
+    def fresh_workspace(self) -> torch.Tensor:
+        """A new sentinel-filled workspace like this one (same device)."""
+        return torch.full_like(self.workspace.view(torch.uint8), SENTINEL_BYTE).view(
+            self.workspace.dtype)
+
+    @property
+    def src_elem_bytes(self) -> int:
+        return self.cache_base.element_size()
+
+    @property
+    def dst_elem_bytes(self) -> int:
+        return self.workspace.element_size()
+
+    def gathered_rows(self) -> int:
+        """Rows the request extents cover (before any guard skips)."""
+        cu = self.cu_seq_lens.cpu().tolist()
+        T = self.num_tokens
+        return sum(max(min(cu[r + 1], T) - min(cu[r], T), 0) for r in range(self.num_reqs))
+
+    def algorithmic_bytes(self) -> int:
+        """Payload read + payload written + metadata read, for a full (unguarded) gather."""
+        rows = self.gathered_rows()
+        pay = rows * self.entry * (self.src_elem_bytes + self.dst_elem_bytes)
+        meta = 4 * (self.num_reqs + 1) + (4 * self.num_reqs if self.seq_starts is not None else 0)
+        return pay + meta
+
+
+# ---------------------------------------------------------------------------
+# drawing helpers
+# ---------------------------------------------------------------------------
+
+def fp8_nonnan_codes(gen: torch.Generator, shape) -> torch.Tensor:
+    """uint8 codes uniform over the 254 e4m3fn codes that are not NaN."""
+    idx = torch.randint(0, 254, shape, generator=gen, dtype=torch.uint8)
+    # indices 0..126 -> codes 0x00..0x7E, 127..253 -> codes 0x80..0xFE
+    return idx + (idx >= 127).to(torch.uint8)
+
+
+def bf16_normal(gen: torch.Generator, shape) -> torch.Tensor:
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def deal_block_table(gen: torch.Generator, context_lens, block_size: int, num_blocks: int,
+                     width: Optional[int] = None, allow_alias: bool = False) -> torch.Tensor:
+    """int32 [R, W]: distinct physical blocks from one randperm, -1 in unused slots.
+
+    With ``allow_alias`` each row is an independent ``randperm`` prefix, so rows
+    may share physical blocks (legal: the gather only reads the cache).
+    """
+    pages = [-(-int(n) // block_size) for n in context_lens]
+    W = max(pages + [1]) if width is None else width
+    assert W >= max(pages + [0])
+    bt = torch.full((len(context_lens), W), -1, dtype=torch.int32)
+    if allow_alias:
+        for r, p in enumerate(pages):
+            assert p <= num_blocks
+            bt[r, :p] = torch.randperm(num_blocks, generator=gen)[:p].to(torch.int32)
+        return bt
+    assert sum(pages) <= num_blocks, (sum(pages), num_blocks)
+    perm = torch.randperm(num_blocks, generator=gen).to(torch.int32)
+    off = 0
+    for r, p in enumerate(pages):
+        bt[r, :p] = perm[off: off + p]
+        off += p
+    return bt
+
+
+def prefix_sums(rows) -> torch.Tensor:
+    cu = [0]
+    for n in rows:
+        cu.append(cu[-1] + int(n))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def make_workload(name: str, kind: str, context_lens, block_size: int, entry: int,
+                  num_blocks: int, seed: int, *, starts=None, width: Optional[int] = None,
+                  cache_cols: Optional[int] = None, dst_cols: Optional[int] = None,
+                  workspace_rows: Optional[int] = None, num_tokens: Optional[int] = None,
+                  scale: float = 1.0, gen: Optional[torch.Generator] = None,
+                  allow_alias: bool = False, draw_starts_quarter: bool = False,
+                  cache_dtype: torch.dtype = torch.bfloat16) -> Workload:
+    """Build one workload.  ``starts``: explicit list, or None; with
+    ``draw_starts_quarter`` each start is drawn uniformly from [0, len // 4].
+    ``cache_dtype`` (raw kinds only): bf16 / fp32 values from N(0,1), or uint8
+    random bytes; the destination has the same dtype.  fp8 kinds always hold
+    e4m3fn codes in a uint8 cache and write bf16."""
+    if gen is None:
+        gen = torch.Generator("cpu").manual_seed(seed)
+    context_lens = [int(x) for x in context_lens]
+    R = len(context_lens)
+    if draw_starts_quarter:
+        starts = [int(torch.randint(0, n // 4 + 1, (1,), generator=gen).item())
+                  for n in context_lens]
+    bt = deal_block_table(gen, context_lens, block_size, num_blocks, width, allow_alias)
+    cache_cols = entry if cache_cols is None else cache_cols
+    dst_cols = entry if dst_cols is None else dst_cols
+    cshape = (num_blocks, block_size, cache_cols)
+    if kind in FP8_KINDS:
+        cache = fp8_nonnan_codes(gen, cshape)
+        dst_dtype = torch.bfloat16
+    elif kind == DEQUANT_AUTO or cache_dtype == torch.bfloat16:
+        cache = bf16_normal(gen, cshape)
+        dst_dtype = torch.bfloat16
+    elif cache_dtype == torch.float32:
+        cache = torch.randn(cshape, generator=gen, dtype=torch.float32)
+        dst_dtype = torch.float32
+    elif cache_dtype == torch.uint8:
+        cache = torch.randint(0, 256, cshape, generator=gen, dtype=torch.uint8)
+        dst_dtype = torch.uint8
+    else:
+        raise ValueError(f"unsupported cache dtype {cache_dtype}")
+    if starts is None:
+        rows = context_lens
+        seq_starts = None
+    else:
+        assert len(starts) == R
+        rows = [max(n - s, 0) for n, s in zip(context_lens, starts)]
+        seq_starts = torch.tensor(starts, dtype=torch.int32)
+    cu = prefix_sums(rows)
+    T = int(cu[-1]) if num_tokens is None else num_tokens
+    ws_rows = T if workspace_rows is None else workspace_rows
+    assert ws_rows >= T
+    esz = torch.empty(0, dtype=dst_dtype).element_size()
+    workspace = torch.full((ws_rows, dst_cols * esz), SENTINEL_BYTE, dtype=torch.uint8).view(
+        dst_dtype)
+    wl = Workload(name=name, kind=kind, block_size=block_size, entry=entry, cache_base=cache,
+                  workspace=workspace, num_tokens=T, block_table=bt, cu_seq_lens=cu,
+                  seq_starts=seq_starts, context_lens=context_lens, scale=scale)
+    if kind in FP8_KINDS:
+        wl.scale_tensor = torch.tensor([scale], dtype=torch.float32)
+    return wl
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads
+# ---------------------------------------------------------------------------
+
+def _lognormal_lengths(gen, n, median, sigma, lo, hi):
+    z = torch.randn(n, generator=gen, dtype=torch.float64)
+    lens = torch.exp(z * sigma + math.log(median)).round().clamp(lo, hi)
+    return [int(x) for x in lens.tolist()]
+
+
+def tiny_raw() -> Workload:
+    """3 requests of {17, 71, 0} tokens, block 16, entry 576 bf16, 32 blocks, table [3, 8]."""
+    return make_workload("tiny_raw", RAW, [17, 71, 0], 16, 576, 32, seed=1001, width=8)
+
+
+def single_60k_raw() -> Workload:
+    """1 request of 61440 tokens (960 pages of 64), entry 576 bf16, 1200 cache blocks."""
+    return make_workload("single_60k_raw", RAW, [61440], 64, 576, 1200, seed=1002)
+
+
+def single_300k_upconvert() -> Workload:
+    """1 request of 307200 tokens (4800 pages of 64), 576 fp8 bytes per entry, 6000 blocks,
+    per-tensor scale 0.0625, fp8 -> bf16 upconvert."""
+    return make_workload("single_300k_fp8_upconvert", UPCONVERT, [307200], 64, 576, 6000,
+                         seed=1003, scale=0.0625)
+
+
+SKEW8_LENS = [131072, 16384, 4096, 1024, 257, 71, 17, 0]
+
+
+def skew8_raw_starts() -> Workload:
+    """8 requests {131072 ... 0}, seq_start uniform in [0, len/4], block 64, entry 576 bf16,
+    3000 blocks, table width 2048; dst = workspace[:T] of a sum(len)-row workspace."""
+    return make_workload("skew8_raw_seq_starts", RAW, SKEW8_LENS, 64, 576, 3000, seed=1004,
+                         width=2048, draw_starts_quarter=True,
+                         workspace_rows=sum(SKEW8_LENS))
+
+
+def mixed_dequant_strided() -> Workload:
+    """64 requests with log-normal lengths (median 4096, sigma 0.5, clipped to [0, 65536]),
+    block 64, fp8 cache rows of 577 bytes using the first 576, scale 0.05, dequantised into
+    a bf16 workspace whose rows are 580 elements wide."""
+    gen = torch.Generator("cpu").manual_seed(1005)
+    lens = _lognormal_lengths(gen, 64, 4096, 0.5, 0, 65536)
+    pages = sum(-(-n // 64) for n in lens)
+    nb = -(-pages * 5 // 4)
+    return make_workload("mixed_fp8_dequant_strided", DEQUANT_FP8, lens, 64, 576, nb, seed=1005,
+                         gen=gen, cache_cols=577, dst_cols=580, scale=0.05,
+                         workspace_rows=sum(lens) + 16)
+
+
+NAMED = {
+    "tiny_raw": tiny_raw,
+    "single_60k_raw": single_60k_raw,
+    "single_300k_fp8_upconvert": single_300k_upconvert,
+    "skew8_raw_seq_starts": skew8_raw_starts,
+    "mixed_fp8_dequant_strided": mixed_dequant_strided,
+}
+
+
+def named(name: str) -> Workload:
+    return NAMED[name]()
