@@ -1,0 +1,279 @@
+"""Benchmark of the paged MLA KV-cache gather on one MI355X.
+
+One step = one call of the library on one batch (all of the hot path: page-task
+build, block lookup, page copy / dequant), inputs already resident in HBM.
+Default workload: one request of 61,440 tokens (960 pages of 64), 576 bf16 per
+token, shuffled physical blocks, raw copy.  Metric: effective HBM GB/s
+(algorithmic bytes read + written per step / time per step).
+
+Cold-cache measurement: the timed steps rotate over several copies of the
+inputs and outputs whose total is far above the 256 MB Infinity Cache, so no
+step finds its data in a cache.  Printed on stdout: ONE JSON line.  Progress
+goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+DEFAULT_WORKLOAD = "single_60k_raw"
+TRAFFIC_DIR = os.path.join(REPO, "profiles")
+KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp",
+                  "paged_kv_cache_device_amd/csrc/pkvg_capi.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(REPO, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def call_for(wl, ws):
+    """The library call for workload ``wl`` into workspace ``ws``, marshalled once."""
+    import paged_kv_cache_device_amd as pkvg
+    import workloads
+
+    dst = ws[: wl.num_tokens, : wl.entry]
+    common = (wl.src_cache(), dst, wl.block_table, wl.cu_seq_lens, wl.num_reqs)
+    if wl.kind == workloads.RAW:
+        return pkvg.prepare("gather_cache", *common, wl.seq_starts)
+    if wl.kind == workloads.UPCONVERT:
+        return pkvg.prepare("gather_upconvert_fp8", *common, wl.scale_tensor,
+                            seq_starts=wl.seq_starts)
+    if wl.kind == workloads.DEQUANT_FP8:
+        return pkvg.prepare("gather_maybe_dequant", *common, "fp8", scale=wl.scale_tensor,
+                            seq_starts=wl.seq_starts)
+    return pkvg.prepare("gather_maybe_dequant", *common, "auto", seq_starts=wl.seq_starts)
+
+
+def make_sets(wl_dev, min_bytes: int):
+    """Copies of (cache, workspace) on the device totalling >= min_bytes."""
+    import dataclasses
+
+    per = wl_dev.cache_base.numel() * wl_dev.cache_base.element_size() + \
+        wl_dev.workspace.numel() * wl_dev.workspace.element_size()
+    n = max(2, -(-min_bytes // per))
+    sets = []
+    for i in range(n):
+        w = dataclasses.replace(wl_dev)
+        if i:
+            w.cache_base = wl_dev.cache_base.clone()
+            w.workspace = wl_dev.workspace.clone()
+        sets.append(w)
+    return sets
+
+
+def time_steps(sets, steps: int, warmup: int, with_events: bool):
+    """Wall time of `steps` back-to-back calls rotating over `sets`, and, with
+    events, the per-launch GPU durations (ms) from events on the launch stream."""
+    import torch
+
+    runs = [call_for(w, w.workspace) for w in sets]
+    for i in range(warmup):
+        runs[i % len(runs)]()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)] if with_events else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        k = i % len(sets)
+        if evs:
+            evs[i][0].record()
+        runs[k]()
+        if evs:
+            evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) for a, b in evs] if evs else None
+    return wall, durs
+
+
+def cold_latency(wl_dev, reps: int, scrub_bytes: int = 1 << 30):
+    """Median / p10 / p90 (us) of one call after scrubbing >= 1 GiB (4x the
+    Infinity Cache) with a fill kernel, bracketed by events on the launch stream."""
+    import torch
+
+    scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=wl_dev.workspace.device)
+    run = call_for(wl_dev, wl_dev.workspace)
+    out = []
+    for i in range(reps + 3):
+        scrub.fill_(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        b.synchronize()
+        if i >= 3:
+            out.append(a.elapsed_time(b) * 1e3)
+    out.sort()
+    return {"median_us": statistics.median(out), "p10_us": out[len(out) // 10],
+            "p90_us": out[(9 * len(out)) // 10], "reps": reps}
+
+
+def copy_reference(nbytes_each_way: int, device, steps: int, min_bytes: int):
+    """A plain device-to-device copy of the same payload (torch copy kernel),
+    cold by rotation: the achievable-copy reference."""
+    import torch
+
+    n = max(2, -(-min_bytes // (2 * nbytes_each_way)))
+    bufs = [(torch.empty(nbytes_each_way, dtype=torch.uint8, device=device),
+             torch.empty(nbytes_each_way, dtype=torch.uint8, device=device)) for _ in range(n)]
+    for s, d in bufs:
+        d.copy_(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s, d = bufs[i % n]
+        d.copy_(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"gbs": 2 * nbytes_each_way * steps / wall / 1e9, "ms_per_copy": wall / steps * 1e3,
+            "bytes_each_way": nbytes_each_way}
+
+
+def cpu_baseline(wl, seconds: float = 10.0):
+    """The CPU oracle (test infrastructure, untuned) on the same workload on
+    the host, single-threaded, repeated for about `seconds`."""
+    import oracle
+
+    oracle.load()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.run_workload(wl)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / reps
+    return {"value": wl.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole workload ({wl.name}), {reps} repetitions in {el:.1f} s, "
+                      f"{per * 1e3:.1f} ms each, one thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--only-gather", action="store_true",
+                    help="run warmup + steps of the gather and nothing else (for profilers)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cold-reps", type=int, default=100)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the gather "
+              "shards by request or page range with no exchange, and multi-GPU runs are "
+              "not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    import paged_kv_cache_device_amd as pkvg
+
+    pkvg.library()
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {args.workload}: generating")
+    wl = workloads.named(args.workload)
+    g = wl.to(dev)
+    alg_bytes = wl.algorithmic_bytes()
+    sets = make_sets(g, 3 << 30)  # far above the 256 MB Infinity Cache
+    log(f"[bench] {len(sets)} input/output copies; algorithmic bytes/step {alg_bytes}")
+
+    if args.only_gather:
+        wall, _ = time_steps(sets, args.steps, args.warmup, with_events=False)
+        log(f"[bench] only-gather: {args.steps} steps in {wall * 1e3:.2f} ms")
+        return
+
+    # the timed region: exactly `steps` calls, events around each launch
+    wall, durs = time_steps(sets, args.steps, args.warmup, with_events=True)
+    ms_per_step = wall / args.steps * 1e3
+    value = alg_bytes / (wall / args.steps) / 1e9
+    kern_ms = statistics.mean(durs)
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step wall, "
+        f"{kern_ms * 1e3:.2f} us/launch (events), {value:.0f} GB/s")
+
+    # warm (same buffers back to back) and cold-with-scrub single calls
+    wall_w, durs_w = time_steps(sets[:1], args.steps, args.warmup, with_events=True)
+    cold = cold_latency(g, args.cold_reps)
+    log(f"[bench] cold scrubbed median {cold['median_us']:.2f} us; warm "
+        f"{statistics.median(durs_w) * 1e3:.2f} us")
+    payload_each_way = wl.gathered_rows() * wl.entry * wl.dst_elem_bytes
+    copy_ref = copy_reference(payload_each_way, dev, args.steps, 3 << 30)
+    log(f"[bench] device copy reference {copy_ref['gbs']:.0f} GB/s")
+
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": "effective HBM GB/s (read+write), cold cache",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.kind == workloads.RAW else "fp8->bf16",
+        "data": "synthetic (seeded N(0,1) bf16 / uniform non-NaN e4m3fn codes; shuffled blocks)",
+        "config": {"workload": wl.name, "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
+                   "block_size": wl.block_size, "entry": wl.entry,
+                   "num_blocks": wl.num_blocks, "kind": wl.kind,
+                   "algorithmic_bytes_per_step": alg_bytes,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
+        "latency_us": {"cold_scrubbed": {k: round(v, 3) for k, v in cold.items()},
+                       "rotating_per_launch_mean": round(kern_ms * 1e3, 3),
+                       "warm_per_launch_median": round(statistics.median(durs_w) * 1e3, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+        "copy_reference": copy_ref,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle (about 10 s)")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,277 @@
+"""paged_kv_cache_device_amd -- paged MLA KV-cache gather on AMD Instinct MI355X.
+
+Thin Python binding over ``libpkvg.so`` (C ABI in ``include/pkvg.h``).  This
+module only marshals torch tensors into pointers, sizes and strides and passes
+the current HIP stream; every step of the gather runs in the library's HIP
+kernels.  torch is used for device memory and streams only.  There is no CPU
+or PyTorch fallback: if the library is missing or a call fails, an exception
+is raised.
+
+Entry points (names as in the C ABI):
+
+* ``gather_cache(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts=None)``
+* ``gather_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size,
+  kv_cache_dtype, scale=None, seq_starts=None)``
+* ``gather_upconvert_fp8(src_cache, dst, block_table, cu_seq_lens, batch_size, scale,
+  seq_starts=None)``
+* ``gather_page_tasks(cu_seq_lens, seq_starts, batch_size, num_tokens, block_size,
+  block_table, num_blocks, capacity=None)``
+
+``src_cache`` is a [num_blocks, block_size, entry] view (innermost stride 1;
+a view of wider rows is fine), ``dst`` a [num_tokens, entry] view (innermost
+stride 1), ``block_table`` int32 [batch, width] (row stride >= width),
+``cu_seq_lens`` int32 [batch + 1], ``seq_starts`` int32 [batch] or None.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # imported first: the library binds to the HIP runtime torch has loaded
+
+from . import build as _build
+
+LIBRARY = _build.LIBRARY
+
+PKVG_OK = 0
+PKVG_E_NULL = 1
+PKVG_E_SHAPE = 2
+PKVG_E_STRIDE = 3
+PKVG_E_DTYPE = 4
+PKVG_E_LIMIT = 5
+PKVG_E_HIP = 6
+PKVG_KV_AUTO = 0
+PKVG_KV_FP8_E4M3 = 1
+PKVG_TASK_INTS = 8
+
+# the C entry points and their argument types, as declared in include/pkvg.h
+_i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_CACHE_ARGS = [_i64, _i32, _i32, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _vp, _i32]
+SIGNATURES = {
+    "gather_cache": [_vp, _i32] + _CACHE_ARGS + [_vp],
+    "gather_maybe_dequant": [_vp, _i32] + _CACHE_ARGS + [_vp, _vp],
+    "gather_upconvert_fp8": [_vp] + _CACHE_ARGS + [_vp, _vp],
+    "gather_page_tasks": [_vp, _vp, _i32, _i64, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp],
+    "pkvg_status_string": [ctypes.c_int],
+    "pkvg_last_hip_error": [],
+}
+
+
+class PkvgError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {status_string(status)}"
+        if status == PKVG_E_HIP:
+            msg += f" (hipError {library().pkvg_last_hip_error()})"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def library(path: str | None = None) -> ctypes.CDLL:
+    """Load ``libpkvg.so`` (built in-tree by ``__graft_entry__.build()`` or
+    ``python -m paged_kv_cache_device_amd.build``).  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY
+    if not os.path.exists(p):
+        raise ImportError(
+            f"{p} is not built; run `python -m paged_kv_cache_device_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(p)
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "pkvg_status_string" else ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().pkvg_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != PKVG_OK:
+        raise PkvgError(status, where)
+
+
+def _stream_handle() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _device_i32(t: torch.Tensor | None, name: str, dim: int) -> torch.Tensor | None:
+    if t is None:
+        return None
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D")
+    if dim == 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
+    if dim == 2 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit innermost stride")
+    return t
+
+
+def _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts):
+    for name, t, d in (("src_cache", src_cache, 3), ("dst", dst, 2)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != d:
+            raise ValueError(f"{name} must be {d}-D")
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name} must have unit innermost stride")
+    _device_i32(block_table, "block_table", 2)
+    _device_i32(cu_seq_lens, "cu_seq_lens", 1)
+    _device_i32(seq_starts, "seq_starts", 1)
+    num_blocks, block_size, entry = src_cache.shape
+    if dst.shape[1] != entry:
+        raise ValueError(f"dst has {dst.shape[1]} columns, cache rows gather {entry}")
+    if cu_seq_lens.numel() < batch_size + 1:
+        raise ValueError("cu_seq_lens needs batch_size + 1 entries")
+    if block_table.shape[0] < batch_size:
+        raise ValueError("block_table needs batch_size rows")
+    if seq_starts is not None and seq_starts.numel() < batch_size:
+        raise ValueError("seq_starts needs batch_size entries")
+    return [num_blocks, block_size, entry, src_cache.stride(0), src_cache.stride(1),
+            _ptr(dst), dst.shape[0], dst.stride(0), _ptr(block_table), block_table.shape[1],
+            block_table.stride(0), _ptr(cu_seq_lens), _ptr(seq_starts), batch_size]
+
+
+class PreparedCall:
+    """A library call with its arguments already marshalled (pointers, sizes,
+    strides and the stream), for loops that issue the same gather many times.
+    Calling it enqueues the gather; the tensors it was prepared from must stay
+    alive and unchanged in shape."""
+
+    def __init__(self, name: str, args: list):
+        self._fn = getattr(library(), name)
+        self._args = args
+        self._name = name
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status != PKVG_OK:
+            raise PkvgError(status, self._name)
+
+
+def _prepare_cache(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts, stream):
+    if src_cache.element_size() != dst.element_size():
+        raise TypeError("gather_cache copies bits: cache and dst element sizes must match")
+    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts)
+    return PreparedCall("gather_cache", [_ptr(src_cache), src_cache.element_size(), *args,
+                                         _stream_handle() if stream is None else stream])
+
+
+def _fp8_source(src_cache: torch.Tensor) -> None:
+    if src_cache.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"an fp8 cache must be uint8 or float8_e4m3fn, got {src_cache.dtype}")
+
+
+def _scale_tensor(scale) -> torch.Tensor:
+    if not isinstance(scale, torch.Tensor) or scale.dtype != torch.float32 or not scale.is_cuda:
+        raise TypeError("scale must be a float32 device tensor with one element")
+    if scale.numel() < 1:
+        raise ValueError("scale must hold one element")
+    return scale
+
+
+def _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size, kv_cache_dtype,
+                           scale, seq_starts, stream):
+    if dst.dtype != torch.bfloat16:
+        raise TypeError("gather_maybe_dequant writes a bf16 destination")
+    if kv_cache_dtype == "auto":
+        if src_cache.dtype != torch.bfloat16:
+            raise TypeError("kv_cache_dtype 'auto' needs a bf16 cache")
+        code, sc = PKVG_KV_AUTO, None
+    elif kv_cache_dtype in ("fp8", "fp8_e4m3"):
+        _fp8_source(src_cache)
+        code, sc = PKVG_KV_FP8_E4M3, _scale_tensor(scale)
+    else:
+        raise ValueError(f"unknown kv_cache_dtype {kv_cache_dtype!r}")
+    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts)
+    return PreparedCall("gather_maybe_dequant", [_ptr(src_cache), code, *args, _ptr(sc),
+                                                 _stream_handle() if stream is None else stream])
+
+
+def _prepare_upconvert(src_cache, dst, block_table, cu_seq_lens, batch_size, scale, seq_starts,
+                       stream):
+    if dst.dtype != torch.bfloat16:
+        raise TypeError("gather_upconvert_fp8 writes a bf16 destination")
+    _fp8_source(src_cache)
+    sc = _scale_tensor(scale)
+    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts)
+    return PreparedCall("gather_upconvert_fp8", [_ptr(src_cache), *args, _ptr(sc),
+                                                 _stream_handle() if stream is None else stream])
+
+
+def gather_cache(src_cache: torch.Tensor, dst: torch.Tensor, block_table: torch.Tensor,
+                 cu_seq_lens: torch.Tensor, batch_size: int,
+                 seq_starts: torch.Tensor | None = None) -> None:
+    """Raw gather: dst rows = cache rows, bit for bit (same element size)."""
+    _prepare_cache(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts, None)()
+
+
+def gather_maybe_dequant(src_cache: torch.Tensor, dst: torch.Tensor, block_table: torch.Tensor,
+                         cu_seq_lens: torch.Tensor, batch_size: int, kv_cache_dtype: str,
+                         scale: torch.Tensor | None = None,
+                         seq_starts: torch.Tensor | None = None) -> None:
+    """Gather into a bf16 dst; kv_cache_dtype 'auto' copies a bf16 cache,
+    'fp8' dequantises e4m3fn codes with the per-tensor fp32 ``scale``."""
+    _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size, kv_cache_dtype,
+                           scale, seq_starts, None)()
+
+
+def gather_upconvert_fp8(src_cache: torch.Tensor, dst: torch.Tensor, block_table: torch.Tensor,
+                         cu_seq_lens: torch.Tensor, batch_size: int, scale: torch.Tensor,
+                         seq_starts: torch.Tensor | None = None) -> None:
+    """fp8 (e4m3fn) cache -> bf16 dst: bf16_rne(fp32(code) * scale)."""
+    _prepare_upconvert(src_cache, dst, block_table, cu_seq_lens, batch_size, scale, seq_starts,
+                       None)()
+
+
+def prepare(entry_point: str, *args, **kwargs) -> PreparedCall:
+    """Marshal the arguments of ``gather_cache`` / ``gather_maybe_dequant`` /
+    ``gather_upconvert_fp8`` once, on the current stream; returns a callable."""
+    stream = None
+    if entry_point == "gather_cache":
+        return _prepare_cache(*args, **kwargs, stream=stream)
+    if entry_point == "gather_maybe_dequant":
+        kwargs.setdefault("scale", None)
+        kwargs.setdefault("seq_starts", None)
+        return _prepare_maybe_dequant(*args, **kwargs, stream=stream)
+    if entry_point == "gather_upconvert_fp8":
+        kwargs.setdefault("seq_starts", None)
+        return _prepare_upconvert(*args, **kwargs, stream=stream)
+    raise ValueError(entry_point)
+
+
+def gather_page_tasks(cu_seq_lens: torch.Tensor, seq_starts: torch.Tensor | None,
+                      batch_size: int, num_tokens: int, block_size: int,
+                      block_table: torch.Tensor, num_blocks: int,
+                      capacity: int | None = None):
+    """Run the page-task builder alone.  Returns (tasks int32 [capacity, 8],
+    count int32 [1]), both on the device; rows past count are unspecified."""
+    _device_i32(block_table, "block_table", 2)
+    _device_i32(cu_seq_lens, "cu_seq_lens", 1)
+    _device_i32(seq_starts, "seq_starts", 1)
+    if capacity is None:
+        capacity = num_tokens // block_size + 2 * batch_size + 1
+    dev = cu_seq_lens.device
+    tasks = torch.empty((max(capacity, 1), PKVG_TASK_INTS), dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(library().gather_page_tasks(
+        _ptr(cu_seq_lens), _ptr(seq_starts), batch_size, num_tokens, block_size,
+        _ptr(block_table), block_table.shape[1], block_table.stride(0), num_blocks,
+        _ptr(tasks), capacity, _ptr(count), _stream_handle()), "gather_page_tasks")
+    return tasks[:capacity], count

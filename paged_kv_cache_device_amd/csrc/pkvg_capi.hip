@@ -1,0 +1,339 @@
+// pkvg_capi.hip -- host side of libpkvg.so: argument validation, access-width
+// and layout selection, launch.  The C ABI is declared in include/pkvg.h.
+//
+// Every argument check happens before the first HIP call, so a rejected call
+// enqueues nothing and touches no device.  Nothing here synchronises with the
+// device; launches go to the caller's stream.
+#include "pkvg.h"
+#include "gather_kernels.hpp"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+using pkvg::GatherParams;
+using pkvg::TaskRecord;
+
+thread_local int g_last_hip_error = 0;
+
+// Workgroups launched for the fused path: one per task (up to this cap); any
+// grid is correct because workgroups stride over tasks.
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return PKVG_E_HIP;
+}
+
+uint32_t magic_for(uint32_t d) {
+  if (d <= 1) return 0xFFFFFFFFu;
+  return static_cast<uint32_t>(((uint64_t(1) << 32) + d - 1) / d);
+}
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % static_cast<uint64_t>(a)) == 0; }
+
+// A validated gather, strides in bytes.
+struct Plan {
+  GatherParams p{};
+  int convert = pkvg::kCopy;
+  int width = 1;          // bytes per lane access (copy) or codes per lane access (fp8)
+  int layout = pkvg::kRows;
+  bool src_vec = true;
+  int64_t capacity = 0;   // upper bound on the number of page tasks
+};
+
+// Checks shared by every gather entry point.  Returns PKVG_OK and fills `plan`,
+// or an error code; `*nothing` is set when there is no work.
+int check_common(const void* src, int64_t num_blocks, int32_t block_size, int32_t entry,
+                 int64_t src_block_stride, int64_t src_token_stride, void* dst,
+                 int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
+                 int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
+                 int32_t num_reqs, bool* nothing) {
+  *nothing = false;
+  if (num_reqs < 0 || num_tokens < 0 || num_blocks < 0 || block_table_width < 0) return PKVG_E_SHAPE;
+  if (block_size <= 0 || entry <= 0) return PKVG_E_SHAPE;
+  if (src_block_stride < 0 || src_token_stride < 0 || dst_row_stride < entry ||
+      block_table_ld < block_table_width)
+    return PKVG_E_STRIDE;
+  if (num_reqs == 0 || num_tokens == 0) {
+    *nothing = true;
+    return PKVG_OK;
+  }
+  if (!src || !dst || !block_table || !cu_seq_lens) return PKVG_E_NULL;
+  // page tasks: at most floor(T / bs) + 2 per request (non-decreasing cu_seq_lens)
+  const int64_t capacity = num_tokens / block_size + 2 * int64_t(num_reqs) + 1;
+  if (capacity >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  return PKVG_OK;
+}
+
+int64_t max_bytes_stride(int64_t stride, int64_t elem) {
+  return stride > INT64_MAX / elem ? -1 : stride * elem;
+}
+
+template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
+  hipLaunchKernelGGL((pkvg::gather_pages_kernel<CONVERT, W, LAYOUT, SRC_VEC>), dim3(grid),
+                     dim3(pkvg::kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int CONVERT, int W, bool SRC_VEC>
+hipError_t launch_layout(const Plan& pl, unsigned grid, size_t lds, hipStream_t stream) {
+  if (pl.layout == pkvg::kFlat) return launch_gather<CONVERT, W, pkvg::kFlat, SRC_VEC>(pl.p, grid, lds, stream);
+  return launch_gather<CONVERT, W, pkvg::kRows, SRC_VEC>(pl.p, grid, lds, stream);
+}
+
+hipError_t dispatch(const Plan& pl, unsigned grid, size_t lds, hipStream_t stream) {
+  if (pl.convert == pkvg::kCopy) {
+    switch (pl.width) {
+      case 16: return launch_layout<pkvg::kCopy, 16, true>(pl, grid, lds, stream);
+      case 8: return launch_layout<pkvg::kCopy, 8, true>(pl, grid, lds, stream);
+      case 4: return launch_layout<pkvg::kCopy, 4, true>(pl, grid, lds, stream);
+      case 2: return launch_layout<pkvg::kCopy, 2, true>(pl, grid, lds, stream);
+      default: return launch_layout<pkvg::kCopy, 1, true>(pl, grid, lds, stream);
+    }
+  }
+  if (pl.src_vec) {
+    switch (pl.width) {
+      case 8: return launch_layout<pkvg::kFp8Bf16, 8, true>(pl, grid, lds, stream);
+      case 4: return launch_layout<pkvg::kFp8Bf16, 4, true>(pl, grid, lds, stream);
+      case 2: return launch_layout<pkvg::kFp8Bf16, 2, true>(pl, grid, lds, stream);
+      default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, grid, lds, stream);
+    }
+  }
+  switch (pl.width) {
+    case 8: return launch_layout<pkvg::kFp8Bf16, 8, false>(pl, grid, lds, stream);
+    case 4: return launch_layout<pkvg::kFp8Bf16, 4, false>(pl, grid, lds, stream);
+    case 2: return launch_layout<pkvg::kFp8Bf16, 2, false>(pl, grid, lds, stream);
+    default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, grid, lds, stream);
+  }
+}
+
+// Builder for large batches and for gather_page_tasks: P scan, then records.
+hipError_t build_tasks(const GatherParams& p, int32_t* P, int32_t* count, TaskRecord* out,
+                       int64_t capacity, hipStream_t stream) {
+  hipLaunchKernelGGL(pkvg::scan_page_counts_kernel, dim3(1), dim3(pkvg::kScanThreads), 0, stream, p, P,
+                     count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || capacity == 0) return e;
+  const int64_t blocks = (capacity + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+  hipLaunchKernelGGL(pkvg::expand_tasks_kernel, dim3(grid), dim3(256), 0, stream, p, P, out,
+                     static_cast<int32_t>(capacity));
+  return hipGetLastError();
+}
+
+int run_plan(Plan& pl, hipStream_t stream) {
+  const int32_t R = pl.p.num_reqs;
+  if (R <= PKVG_FUSED_MAX_REQS) {
+    const int64_t g = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
+    const size_t lds = sizeof(int32_t) * (3 * size_t(R) + 3);
+    hipError_t e = dispatch(pl, static_cast<unsigned>(g), lds, stream);
+    return e == hipSuccess ? PKVG_OK : hip_fail(e);
+  }
+  // large batch: stream-ordered scratch = P[R+1] | count | records[capacity]
+  const size_t p_bytes = sizeof(int32_t) * (size_t(R) + 2);
+  const size_t rec_off = (p_bytes + 255) / 256 * 256;
+  const size_t bytes = rec_off + sizeof(TaskRecord) * size_t(pl.capacity);
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  int32_t* P = static_cast<int32_t*>(scratch);
+  int32_t* count = P + R + 1;
+  TaskRecord* rec = reinterpret_cast<TaskRecord*>(static_cast<char*>(scratch) + rec_off);
+  e = build_tasks(pl.p, P, count, rec, pl.capacity, stream);
+  if (e == hipSuccess) {
+    pl.p.tasks = rec;
+    pl.p.task_count = count;
+    pl.p.task_capacity = static_cast<int32_t>(pl.capacity);
+    const int64_t g = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
+    e = dispatch(pl, static_cast<unsigned>(g), 0, stream);
+  }
+  const hipError_t ef = hipFreeAsync(scratch, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return PKVG_OK;
+}
+
+void fill_common(Plan& pl, const void* src, void* dst, const int32_t* block_table,
+                 int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
+                 const int32_t* seq_starts, int32_t num_reqs, int64_t num_blocks, int32_t block_size,
+                 int64_t num_tokens) {
+  pl.p.src = static_cast<const uint8_t*>(src);
+  pl.p.dst = static_cast<uint8_t*>(dst);
+  pl.p.block_table = block_table;
+  pl.p.cu_seq_lens = cu_seq_lens;
+  pl.p.seq_starts = seq_starts;
+  pl.p.block_table_ld = block_table_ld;
+  pl.p.block_table_width = block_table_width;
+  pl.p.num_reqs = num_reqs;
+  pl.p.num_blocks = num_blocks;
+  pl.p.block_size = block_size;
+  pl.p.num_tokens = num_tokens;
+  pl.capacity = num_tokens / block_size + 2 * int64_t(num_reqs) + 1;
+}
+
+// Raw copy plan: pick the widest access that every row, stride and base allows.
+int plan_copy(Plan& pl, const void* src, void* dst, int64_t elem, int32_t entry, int64_t sbs,
+              int64_t sts, int64_t drs, int32_t block_size) {
+  const int64_t row = int64_t(entry) * elem;
+  const int64_t sb = max_bytes_stride(sbs, elem), st = max_bytes_stride(sts, elem),
+                dr = max_bytes_stride(drs, elem);
+  if (sb < 0 || st < 0 || dr < 0) return PKVG_E_LIMIT;
+  if (int64_t(block_size) * row >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  int w = 16;
+  while (w > 1 && (row % w || sb % w || st % w || dr % w || !aligned(src, w) || !aligned(dst, w))) w >>= 1;
+  pl.convert = pkvg::kCopy;
+  pl.width = w;
+  pl.layout = (st == row && dr == row) ? pkvg::kFlat : pkvg::kRows;
+  pl.p.src_block_stride = sb;
+  pl.p.src_token_stride = st;
+  pl.p.dst_row_stride = dr;
+  pl.p.chunks_per_row = static_cast<int32_t>(row / w);
+  pl.p.chunks_magic = magic_for(static_cast<uint32_t>(row / w));
+  return PKVG_OK;
+}
+
+// fp8 -> bf16 plan: K codes per lane, limited by the bf16 store alignment (2K
+// bytes) and the row length; byte loads when the code rows are not K-aligned.
+int plan_fp8(Plan& pl, const void* src, void* dst, int32_t entry, int64_t sbs, int64_t sts,
+             int64_t drs_elems, int32_t block_size) {
+  const int64_t dr = max_bytes_stride(drs_elems, 2);
+  if (dr < 0) return PKVG_E_LIMIT;
+  if (int64_t(block_size) * entry * 2 >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  int k = 8;
+  while (k > 1 && (entry % k || dr % (2 * k) || !aligned(dst, 2 * k))) k >>= 1;
+  pl.convert = pkvg::kFp8Bf16;
+  pl.width = k;
+  pl.src_vec = (sbs % k == 0) && (sts % k == 0) && aligned(src, k);
+  pl.layout = (sts == entry && dr == 2 * int64_t(entry)) ? pkvg::kFlat : pkvg::kRows;
+  pl.p.src_block_stride = sbs;
+  pl.p.src_token_stride = sts;
+  pl.p.dst_row_stride = dr;
+  pl.p.chunks_per_row = entry / k;
+  pl.p.chunks_magic = magic_for(static_cast<uint32_t>(entry / k));
+  return PKVG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, int32_t block_size,
+                 int32_t entry, int64_t src_block_stride, int64_t src_token_stride, void* dst,
+                 int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
+                 int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
+                 const int32_t* seq_starts, int32_t num_reqs, void* stream) {
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return PKVG_E_DTYPE;
+  bool nothing;
+  int st = check_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                        num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                        cu_seq_lens, num_reqs, &nothing);
+  if (st != PKVG_OK || nothing) return st;
+  Plan pl;
+  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, seq_starts,
+              num_reqs, num_blocks, block_size, num_tokens);
+  st = plan_copy(pl, src_cache, dst, elem_bytes, entry, src_block_stride, src_token_stride, dst_row_stride,
+                 block_size);
+  if (st != PKVG_OK) return st;
+  return run_plan(pl, static_cast<hipStream_t>(stream));
+}
+
+static int gather_fp8_common(const void* src_cache, int64_t num_blocks, int32_t block_size, int32_t entry,
+                             int64_t src_block_stride, int64_t src_token_stride, void* dst,
+                             int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
+                             int32_t block_table_width, int64_t block_table_ld,
+                             const int32_t* cu_seq_lens, const int32_t* seq_starts, int32_t num_reqs,
+                             const float* scale, void* stream) {
+  bool nothing;
+  int st = check_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                        num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                        cu_seq_lens, num_reqs, &nothing);
+  if (st != PKVG_OK || nothing) return st;
+  if (!scale) return PKVG_E_NULL;
+  Plan pl;
+  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, seq_starts,
+              num_reqs, num_blocks, block_size, num_tokens);
+  pl.p.scale = scale;
+  st = plan_fp8(pl, src_cache, dst, entry, src_block_stride, src_token_stride, dst_row_stride, block_size);
+  if (st != PKVG_OK) return st;
+  return run_plan(pl, static_cast<hipStream_t>(stream));
+}
+
+int gather_maybe_dequant(const void* src_cache, int32_t kv_cache_dtype, int64_t num_blocks,
+                         int32_t block_size, int32_t entry, int64_t src_block_stride,
+                         int64_t src_token_stride, void* dst, int64_t num_tokens, int64_t dst_row_stride,
+                         const int32_t* block_table, int32_t block_table_width, int64_t block_table_ld,
+                         const int32_t* cu_seq_lens, const int32_t* seq_starts, int32_t num_reqs,
+                         const float* scale, void* stream) {
+  if (kv_cache_dtype == PKVG_KV_AUTO)
+    return gather_cache(src_cache, 2, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                        num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                        cu_seq_lens, seq_starts, num_reqs, stream);
+  if (kv_cache_dtype != PKVG_KV_FP8_E4M3) return PKVG_E_DTYPE;
+  return gather_fp8_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                           num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                           cu_seq_lens, seq_starts, num_reqs, scale, stream);
+}
+
+int gather_upconvert_fp8(const void* src_cache, int64_t num_blocks, int32_t block_size, int32_t entry,
+                         int64_t src_block_stride, int64_t src_token_stride, void* dst, int64_t num_tokens,
+                         int64_t dst_row_stride, const int32_t* block_table, int32_t block_table_width,
+                         int64_t block_table_ld, const int32_t* cu_seq_lens, const int32_t* seq_starts,
+                         int32_t num_reqs, const float* scale, void* stream) {
+  return gather_fp8_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                           num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                           cu_seq_lens, seq_starts, num_reqs, scale, stream);
+}
+
+int gather_page_tasks(const int32_t* cu_seq_lens, const int32_t* seq_starts, int32_t num_reqs,
+                      int64_t num_tokens, int32_t block_size, const int32_t* block_table,
+                      int32_t block_table_width, int64_t block_table_ld, int64_t num_blocks, int32_t* tasks,
+                      int64_t capacity, int32_t* num_tasks, void* stream) {
+  if (num_reqs < 0 || num_tokens < 0 || block_size <= 0 || block_table_width < 0 || num_blocks < 0 ||
+      capacity < 0)
+    return PKVG_E_SHAPE;
+  if (block_table_ld < block_table_width) return PKVG_E_STRIDE;
+  if (!num_tasks || (num_reqs > 0 && (!cu_seq_lens || !block_table)) || (capacity > 0 && !tasks))
+    return PKVG_E_NULL;
+  if (capacity >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  if (num_tokens / block_size + 2 * int64_t(num_reqs) + 1 >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GatherParams p{};
+  p.block_table = block_table;
+  p.cu_seq_lens = cu_seq_lens;
+  p.seq_starts = seq_starts;
+  p.block_table_ld = block_table_ld;
+  p.block_table_width = block_table_width;
+  p.num_reqs = num_reqs;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.num_tokens = num_tokens;
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, sizeof(int32_t) * (size_t(num_reqs) + 1), s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = build_tasks(p, static_cast<int32_t*>(scratch), num_tasks, reinterpret_cast<TaskRecord*>(tasks), capacity,
+                  s);
+  const hipError_t ef = hipFreeAsync(scratch, s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ef != hipSuccess) return hip_fail(ef);
+  return PKVG_OK;
+}
+
+const char* pkvg_status_string(int status) {
+  switch (status) {
+    case PKVG_OK: return "PKVG_OK";
+    case PKVG_E_NULL: return "PKVG_E_NULL: a required pointer is NULL";
+    case PKVG_E_SHAPE: return "PKVG_E_SHAPE: a count or size is out of range";
+    case PKVG_E_STRIDE: return "PKVG_E_STRIDE: a stride is negative or rows overlap";
+    case PKVG_E_DTYPE: return "PKVG_E_DTYPE: unsupported element size or kv_cache_dtype";
+    case PKVG_E_LIMIT: return "PKVG_E_LIMIT: beyond an implementation limit";
+    case PKVG_E_HIP: return "PKVG_E_HIP: a HIP runtime call failed";
+    default: return "unknown pkvg status";
+  }
+}
+
+int pkvg_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

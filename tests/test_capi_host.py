@@ -1,0 +1,123 @@
+"""Host-side checks of the C-ABI library that need no GPU: the library loads,
+exports every entry point include/pkvg.h declares, and rejects bad arguments
+(or returns early when there is no work) before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "pkvg.h")
+
+pkvg = pytest.importorskip("paged_kv_cache_device_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_device_amd import build
+
+    if build.is_stale():
+        build.build()
+    return pkvg.library()
+
+
+def test_header_declares_the_entry_points():
+    names = set(_declared_functions())
+    assert {"gather_cache", "gather_maybe_dequant", "gather_upconvert_fp8",
+            "gather_page_tasks", "pkvg_status_string", "pkvg_last_hip_error"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(pkvg.SIGNATURES)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert pkvg.status_string(code).startswith("PKVG_")
+    assert "unknown" in pkvg.status_string(99)
+    assert lib.pkvg_last_hip_error() == 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below returns before any HIP call
+
+
+def _gc(lib, **kw):
+    a = dict(src=FAKE, elem=2, nb=4, bs=16, entry=8, sbs=128, sts=8, dst=FAKE, T=10, drs=8,
+             bt=FAKE, W=2, ld=2, cu=FAKE, ss=None, R=1)
+    a.update(kw)
+    return lib.gather_cache(a["src"], a["elem"], a["nb"], a["bs"], a["entry"], a["sbs"], a["sts"],
+                            a["dst"], a["T"], a["drs"], a["bt"], a["W"], a["ld"], a["cu"], a["ss"],
+                            a["R"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(elem=3), pkvg.PKVG_E_DTYPE),
+    (dict(elem=0), pkvg.PKVG_E_DTYPE),
+    (dict(bs=0), pkvg.PKVG_E_SHAPE),
+    (dict(entry=0), pkvg.PKVG_E_SHAPE),
+    (dict(R=-1), pkvg.PKVG_E_SHAPE),
+    (dict(T=-1), pkvg.PKVG_E_SHAPE),
+    (dict(nb=-1), pkvg.PKVG_E_SHAPE),
+    (dict(W=-1), pkvg.PKVG_E_SHAPE),
+    (dict(drs=7), pkvg.PKVG_E_STRIDE),
+    (dict(sts=-1), pkvg.PKVG_E_STRIDE),
+    (dict(sbs=-1), pkvg.PKVG_E_STRIDE),
+    (dict(ld=1), pkvg.PKVG_E_STRIDE),
+    (dict(src=None), pkvg.PKVG_E_NULL),
+    (dict(dst=None), pkvg.PKVG_E_NULL),
+    (dict(bt=None), pkvg.PKVG_E_NULL),
+    (dict(cu=None), pkvg.PKVG_E_NULL),
+    (dict(T=(1 << 31) * 16), pkvg.PKVG_E_LIMIT),        # too many page tasks
+    (dict(bs=1 << 20, entry=1 << 10, drs=1 << 10), pkvg.PKVG_E_LIMIT),  # a page spans >= 2^31 bytes
+    (dict(R=0, src=None, dst=None, bt=None, cu=None), pkvg.PKVG_OK),   # no work: nothing enqueued
+    (dict(T=0, src=None, dst=None, bt=None, cu=None), pkvg.PKVG_OK),
+])
+def test_gather_cache_argument_checks(lib, kw, code):
+    assert _gc(lib, **kw) == code
+
+
+def test_maybe_dequant_argument_checks(lib):
+    args = [4, 16, 8, 128, 8, FAKE, 10, 8, FAKE, 2, 2, FAKE, None, 1]
+    assert lib.gather_maybe_dequant(FAKE, 7, *args, FAKE, None) == pkvg.PKVG_E_DTYPE
+    assert lib.gather_maybe_dequant(FAKE, pkvg.PKVG_KV_FP8_E4M3, *args, None, None) == pkvg.PKVG_E_NULL
+    assert lib.gather_upconvert_fp8(FAKE, *args, None, None) == pkvg.PKVG_E_NULL
+    no_work = [4, 16, 8, 128, 8, None, 0, 8, None, 2, 2, None, None, 1]
+    assert lib.gather_upconvert_fp8(None, *no_work, None, None) == pkvg.PKVG_OK
+    bad_stride = [4, 16, 8, 128, 8, FAKE, 10, 7, FAKE, 2, 2, FAKE, None, 1]
+    assert lib.gather_upconvert_fp8(FAKE, *bad_stride, FAKE, None) == pkvg.PKVG_E_STRIDE
+
+
+def test_page_tasks_argument_checks(lib):
+    f = lib.gather_page_tasks
+    assert f(FAKE, None, 1, 10, 0, FAKE, 2, 2, 4, FAKE, 8, FAKE, None) == pkvg.PKVG_E_SHAPE
+    assert f(FAKE, None, 1, 10, 16, FAKE, 2, 1, 4, FAKE, 8, FAKE, None) == pkvg.PKVG_E_STRIDE
+    assert f(FAKE, None, 1, 10, 16, FAKE, 2, 2, 4, FAKE, 8, None, None) == pkvg.PKVG_E_NULL
+    assert f(None, None, 1, 10, 16, FAKE, 2, 2, 4, FAKE, 8, FAKE, None) == pkvg.PKVG_E_NULL
+    assert f(FAKE, None, 1, 10, 16, FAKE, 2, 2, 4, None, 8, FAKE, None) == pkvg.PKVG_E_NULL
+    assert f(FAKE, None, 1, 10, 16, FAKE, 2, 2, 4, FAKE, 1 << 31, FAKE, None) == pkvg.PKVG_E_LIMIT
+    assert f(FAKE, None, -1, 10, 16, FAKE, 2, 2, 4, FAKE, 8, FAKE, None) == pkvg.PKVG_E_SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    cache = torch.zeros(4, 16, 8, dtype=torch.bfloat16)
+    dst = torch.zeros(10, 8, dtype=torch.bfloat16)
+    bt = torch.zeros(1, 2, dtype=torch.int32)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pkvg.gather_cache(cache, dst, bt, cu, 1)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        pkvg.library(str(tmp_path / "missing.so"))

@@ -1,0 +1,258 @@
+"""Parity of the HIP gather (through the C ABI) with the CPU oracle, bit for
+bit, on MI355X: the five named workloads at full size, seeded random small
+workloads spanning every edge case, every access-width path, the exhaustive
+fp8 code table, the page-task builder, the large-batch (tabled) path, and byte
+offsets beyond 2^31."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle_pins
+import workloads
+from gpu_util import check_parity, log, run_hip
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_device_amd as pkvg
+
+    pkvg.library()  # fail loudly if the HIP library is missing
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads, full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(workloads.NAMED))
+def test_named_workload_parity(name):
+    check_parity(workloads.named(name), DEV)
+
+
+# ---------------------------------------------------------------------------
+# random small workloads: partial pages, seq_starts, zero-length requests,
+# aliased blocks, strided rows, num_tokens clamping, guard-skipped pages
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_random_small_workloads(seed):
+    for wl in oracle_pins.random_small_workloads(seed, 40):
+        check_parity(wl, DEV)
+
+
+@pytest.mark.parametrize("R,bs", [(64, 16), (300, 16), (1024, 4), (1025, 4), (3000, 2)])
+def test_many_requests(R, bs):
+    """Fused builder with several requests per thread (R > 256), the largest fused
+    batch, and the tabled builder beyond it."""
+    g = torch.Generator("cpu").manual_seed(R)
+    lens = torch.randint(0, 5 * bs, (R,), generator=g)
+    lens[torch.rand(R, generator=g) < 0.15] = 0
+    lens = lens.tolist()
+    starts = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in lens]
+    pages = sum(-(-n // bs) for n in lens)
+    for kind, use_starts in ((workloads.RAW, True), (workloads.UPCONVERT, False)):
+        wl = workloads.make_workload(f"many_{R}_{kind}", kind, lens, bs, 72, pages + 3,
+                                     seed=R + 1, starts=starts if use_starts else None,
+                                     scale=0.05)
+        check_parity(wl, DEV)
+
+
+# ---------------------------------------------------------------------------
+# every access path: widths 16/8/4/2/1 x flat/rows for raw copies; 8/4/2/1
+# codes per lane x vector/byte loads x flat/rows for fp8
+# ---------------------------------------------------------------------------
+
+RAW_PATHS = [
+    # (cache dtype, entry, cache cols, dst cols)
+    (torch.bfloat16, 576, 576, 576),   # 16 B, flat
+    (torch.bfloat16, 576, 640, 576),   # 16 B, rows (padded cache rows)
+    (torch.bfloat16, 576, 576, 584),   # 16 B, rows (padded dst rows)
+    (torch.bfloat16, 12, 12, 12),      # 8 B (24-byte rows), flat
+    (torch.bfloat16, 12, 16, 12),      # 8 B, rows
+    (torch.bfloat16, 6, 6, 6),         # 4 B, flat
+    (torch.bfloat16, 6, 8, 10),        # 4 B, rows
+    (torch.bfloat16, 7, 7, 7),         # 2 B, flat
+    (torch.bfloat16, 7, 9, 8),         # 2 B, rows
+    (torch.uint8, 577, 577, 577),      # 1 B, flat
+    (torch.uint8, 577, 579, 580),      # 1 B, rows
+    (torch.float32, 576, 576, 576),    # fp32 entries, 16 B flat
+    (torch.float32, 3, 5, 3),          # fp32, 4 B rows
+]
+
+
+@pytest.mark.parametrize("dtype,entry,ccols,dcols", RAW_PATHS)
+def test_raw_access_paths(dtype, entry, ccols, dcols):
+    lens = [0, 1, 63, 64, 65, 200, 17]
+    starts = [5, 0, 1, 0, 63, 7, 16]
+    for use_starts in (False, True):
+        wl = workloads.make_workload(f"raw_{dtype}_{entry}_{ccols}_{dcols}", workloads.RAW, lens,
+                                     16, entry, 40, seed=entry + ccols,
+                                     starts=starts if use_starts else None, cache_cols=ccols,
+                                     dst_cols=dcols, cache_dtype=dtype,
+                                     workspace_rows=sum(lens) + 3)
+        check_parity(wl, DEV)
+
+
+FP8_PATHS = [
+    # (entry, cache cols, dst cols)
+    (576, 576, 576),   # 8 codes, vector loads, flat
+    (576, 584, 576),   # 8 codes, vector loads, rows
+    (576, 577, 576),   # 8 codes (dst 16-B aligned), byte loads, rows
+    (576, 577, 580),   # 4 codes, byte loads, rows (the strided mixed workload)
+    (576, 580, 580),   # 4 codes, vector loads, rows
+    (12, 12, 12),      # 4 codes (24-byte dst rows), flat
+    (6, 6, 6),         # 2 codes, flat
+    (6, 7, 7),         # 1 code
+    (5, 5, 5),         # 1 code, flat
+]
+
+
+@pytest.mark.parametrize("entry,ccols,dcols", FP8_PATHS)
+@pytest.mark.parametrize("kind", [workloads.DEQUANT_FP8, workloads.UPCONVERT])
+def test_fp8_access_paths(kind, entry, ccols, dcols):
+    lens = [0, 1, 63, 64, 65, 200, 17]
+    starts = [5, 0, 1, 0, 63, 7, 16]
+    for use_starts in (False, True):
+        wl = workloads.make_workload(f"fp8_{entry}_{ccols}_{dcols}", kind, lens, 16, entry, 40,
+                                     seed=entry * 7 + ccols, starts=starts if use_starts else None,
+                                     cache_cols=ccols, dst_cols=dcols, scale=0.05,
+                                     workspace_rows=sum(lens) + 3)
+        check_parity(wl, DEV)
+
+
+# ---------------------------------------------------------------------------
+# the fp8 arithmetic on every code, NaN codes included
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scale", [0.0625, 0.05, 1.0, 9.7, 0.5395833253860474, -3.0, 1e-38,
+                                   1.7e38, 7.62939453125e-06])
+def test_fp8_every_code(scale):
+    """One block holds all 256 codes; compare with the oracle element by element
+    (bit-exact), NaN codes only for NaN-ness."""
+    import paged_kv_cache_device_amd as pkvg
+
+    log(f"[fp8 codes] scale={scale}")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(1, 4, 64)  # 1 block, bs 4
+    bt = torch.tensor([[0]], dtype=torch.int32)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    sc = torch.tensor([scale], dtype=torch.float32)
+    dst = torch.full((4, 64), -1, dtype=torch.int16).view(torch.bfloat16)
+    o = oracle.load()
+    want = torch.tensor([o.dequant_e4m3fn_bf16(c, scale) for c in range(256)], dtype=torch.int32)
+    d = dst.to(DEV)
+    pkvg.gather_upconvert_fp8(codes.to(DEV), d, bt.to(DEV), cu.to(DEV), 1, sc.to(DEV))
+    torch.cuda.synchronize()
+    got = d.cpu().view(torch.int16).flatten().to(torch.int32) & 0xFFFF
+    nan = torch.tensor([c in (0x7F, 0xFF) for c in range(256)])
+    assert torch.equal(got[~nan], want[~nan]), (got[~nan] != want[~nan]).nonzero().flatten()[:8]
+    assert torch.isnan(d.cpu().flatten().float()[nan]).all()
+
+
+# ---------------------------------------------------------------------------
+# the page-task builder on its own
+# ---------------------------------------------------------------------------
+
+def test_page_tasks_match_oracle():
+    import paged_kv_cache_device_amd as pkvg
+
+    o = oracle.load()
+    g = torch.Generator("cpu").manual_seed(5)
+    for k in range(40):
+        R = int(torch.randint(1, 40 if k % 4 else 1500, (1,), generator=g))
+        bs = [1, 2, 16, 64][k % 4]
+        lens = torch.randint(0, 4 * bs + 3, (R,), generator=g)
+        lens[torch.rand(R, generator=g) < 0.2] = 0
+        starts = torch.randint(0, 3 * bs, (R,), generator=g) if k % 2 else None
+        cu = torch.cat([torch.zeros(1, dtype=torch.int64), lens.cumsum(0)]).to(torch.int32)
+        T = int(cu[-1]) if k % 3 else int(cu[-1]) // 2
+        W = int(((starts if starts is not None else 0) + lens).max()) // bs + 1
+        nb = 50
+        bt = torch.randint(-2, nb + 3, (R, W + 2), generator=g, dtype=torch.int32)
+        log(f"[page tasks] case {k} R={R} bs={bs} T={T} starts={starts is not None}")
+        want = o.page_tasks(cu, None if starts is None else starts.to(torch.int32), R, T, bs)
+        want = want[want[:, 3] > want[:, 2]]  # the method's empty tasks are not built here
+        tasks, count = pkvg.gather_page_tasks(
+            cu.to(DEV), None if starts is None else starts.to(torch.int32).to(DEV), R, T, bs,
+            bt.to(DEV)[:, :W], nb)
+        torch.cuda.synchronize()
+        n = int(count.item())
+        got = tasks[:n].cpu().numpy()
+        assert n == len(want), (k, n, len(want))
+        assert np.array_equal(got[:, :5], want), k
+        btn = bt.numpy()
+        for row in got:
+            r, lb = row[0], row[1]
+            phys = btn[r, lb] if lb < W else -1
+            phys = phys if 0 <= phys < nb else -1
+            assert row[5] == phys
+
+
+# ---------------------------------------------------------------------------
+# no work, block table pitch, byte offsets beyond 2^31
+# ---------------------------------------------------------------------------
+
+def test_no_work_leaves_destination_untouched():
+    import paged_kv_cache_device_amd as pkvg
+
+    cache = torch.randn(4, 16, 8).to(torch.bfloat16).to(DEV)
+    ws = torch.full((10, 8), 7.0, dtype=torch.bfloat16, device=DEV)
+    bt = torch.zeros(1, 2, dtype=torch.int32, device=DEV)
+    cu = torch.tensor([0, 10], dtype=torch.int32, device=DEV)
+    pkvg.gather_cache(cache, ws[:0], bt, cu, 1)          # num_tokens == 0
+    pkvg.gather_cache(cache, ws, bt, cu, 0)              # num_reqs == 0
+    torch.cuda.synchronize()
+    assert bool((ws == 7.0).all())
+
+
+def test_block_table_row_pitch():
+    """A block table that is a column slice of a wider table (row pitch > width)."""
+    import paged_kv_cache_device_amd as pkvg
+
+    wl = workloads.make_workload("pitch", workloads.RAW, [40, 70, 5], 16, 64, 20, seed=3,
+                                 width=5)
+    want, _ = oracle.run_workload(wl)
+    wide = torch.full((3, 9), 12345, dtype=torch.int32)
+    wide[:, :5] = wl.block_table
+    g = wl.to(DEV)
+    ws = g.fresh_workspace()
+    pkvg.gather_cache(g.src_cache(), ws[: g.num_tokens, : g.entry], wide.to(DEV)[:, :5],
+                      g.cu_seq_lens, 3, None)
+    torch.cuda.synchronize()
+    assert torch.equal(ws.cpu().view(torch.uint8), want.view(torch.uint8))
+
+
+def test_offsets_beyond_2_to_31_bytes():
+    """One request of 1,000,000 tokens of fp32 entries (2304-byte rows): output row
+    offsets and physical page offsets both pass 2^31 bytes (the int32 product
+    the page's review flags would overflow near 932K tokens)."""
+    import paged_kv_cache_device_amd as pkvg
+
+    T, bs, entry = 1_000_000, 64, 576
+    nb = T // bs + 1 + 40
+    log(f"[int64] T={T} bytes per side ~{T * entry * 4 / 2**30:.2f} GiB")
+    g = torch.Generator("cpu").manual_seed(64)
+    perm = torch.randperm(nb, generator=g).to(torch.int32)
+    pages = -(-T // bs)
+    bt = perm[:pages].view(1, pages).contiguous()
+    # self-identifying fp32 bit patterns, generated on the device
+    ids = ((torch.arange(nb, device=DEV, dtype=torch.int32).view(nb, 1, 1) << 16)
+           | (torch.arange(bs, device=DEV, dtype=torch.int32).view(1, bs, 1) << 10)
+           | torch.arange(entry, device=DEV, dtype=torch.int32).view(1, 1, entry))
+    cache = ids.view(torch.float32)
+    ws = torch.full((T + 2, entry), -1, dtype=torch.int32, device=DEV).view(torch.float32)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    pkvg.gather_cache(cache, ws[:T], bt.to(DEV), cu.to(DEV), 1, None)
+    torch.cuda.synchronize()
+    got = ws.cpu()
+    del ws
+    want = torch.full((T + 2, entry), -1, dtype=torch.int32).view(torch.float32)
+    o = oracle.load()
+    rows = o.gather_tensors(oracle.MODE_COPY, cache.cpu(), want[:T], bt, cu, None, 1)
+    assert rows == T
+    assert torch.equal(got.view(torch.int32), want.view(torch.int32))
