@@ -93,30 +93,28 @@ def make_sets(wl_dev, min_bytes: int):
     return sets
 
 
-def time_steps(sets, steps: int, warmup: int, with_events: bool):
-    """Wall time of `steps` back-to-back calls rotating over `sets`, and, with
-    events, the per-launch GPU durations (ms) from events on the launch stream."""
+def time_steps(sets, steps: int, warmup: int):
+    """Exactly `steps` back-to-back calls rotating over `sets`, bracketed by
+    torch.cuda.synchronize() on both sides.  Returns the wall time (s) and the
+    GPU time (ms) between two HIP events recorded on the launch stream right
+    before the first and right after the last call."""
     import torch
 
     runs = [call_for(w, w.workspace) for w in sets]
     for i in range(warmup):
         runs[i % len(runs)]()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)] if with_events else None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
-        k = i % len(sets)
-        if evs:
-            evs[i][0].record()
-        runs[k]()
-        if evs:
-            evs[i][1].record()
+        runs[i % len(runs)]()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [a.elapsed_time(b) for a, b in evs] if evs else None
-    return wall, durs
+    return wall, e0.elapsed_time(e1)
 
 
 def cold_latency(wl_dev, reps: int, scrub_bytes: int = 1 << 30):
@@ -216,24 +214,25 @@ def main():
     log(f"[bench] {len(sets)} input/output copies; algorithmic bytes/step {alg_bytes}")
 
     if args.only_gather:
-        wall, _ = time_steps(sets, args.steps, args.warmup, with_events=False)
+        wall, _ = time_steps(sets, args.steps, args.warmup)
         log(f"[bench] only-gather: {args.steps} steps in {wall * 1e3:.2f} ms")
         return
 
-    # the timed region: exactly `steps` calls, events around each launch
-    wall, durs = time_steps(sets, args.steps, args.warmup, with_events=True)
+    # the timed region: exactly `steps` calls; HIP events on the launch stream
+    # around the region give the average launch duration for the roofline
+    wall, ev_ms = time_steps(sets, args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
     value = alg_bytes / (wall / args.steps) / 1e9
-    kern_ms = statistics.mean(durs)
+    kern_ms = ev_ms / args.steps
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step wall, "
         f"{kern_ms * 1e3:.2f} us/launch (events), {value:.0f} GB/s")
 
-    # warm (same buffers back to back) and cold-with-scrub single calls
-    wall_w, durs_w = time_steps(sets[:1], args.steps, args.warmup, with_events=True)
+    # warm (the same buffers back to back) and single calls after a cache scrub
+    _, ev_w = time_steps(sets[:1], args.steps, args.warmup)
+    warm_us = ev_w / args.steps * 1e3
     cold = cold_latency(g, args.cold_reps)
-    log(f"[bench] cold scrubbed median {cold['median_us']:.2f} us; warm "
-        f"{statistics.median(durs_w) * 1e3:.2f} us")
+    log(f"[bench] cold scrubbed median {cold['median_us']:.2f} us; warm {warm_us:.2f} us")
     payload_each_way = wl.gathered_rows() * wl.entry * wl.dst_elem_bytes
     copy_ref = copy_reference(payload_each_way, dev, args.steps, 3 << 30)
     log(f"[bench] device copy reference {copy_ref['gbs']:.0f} GB/s")
@@ -259,9 +258,10 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
-        "latency_us": {"cold_scrubbed": {k: round(v, 3) for k, v in cold.items()},
-                       "rotating_per_launch_mean": round(kern_ms * 1e3, 3),
-                       "warm_per_launch_median": round(statistics.median(durs_w) * 1e3, 3)},
+        "per_launch_us": round(kern_ms * 1e3, 3),
+        "latency_us": {"cold_scrubbed_single_call": {k: round(v, 3) for k, v in cold.items()},
+                       "back_to_back_per_launch_cold": round(kern_ms * 1e3, 3),
+                       "back_to_back_per_launch_warm": round(warm_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},

@@ -18,7 +18,7 @@
 //    block in SGPRs (readfirstlane), so no second barrier is needed;
 //  * the hot loop moves 16-byte (dwordx4) chunks, consecutive lanes on
 //    consecutive chunks, so one wave instruction covers 1 KiB of a row span;
-//    kUnroll loads are in flight per lane before the matching stores;
+//    a whole page's loads are in flight before the matching stores;
 //  * all addressing that can exceed 2^31 bytes (page bases, output row bases)
 //    is int64; in-page offsets are 32-bit (the host guarantees that a page's
 //    rows span < 2^31 bytes);
@@ -32,18 +32,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pkvg {
 
-#ifndef PKVG_THREADS
-#define PKVG_THREADS 256
-#endif
-#ifndef PKVG_UNROLL
-#define PKVG_UNROLL 8
-#endif
+// Workgroup shapes: threads per workgroup and chunks per lane per batch.  A
+// batch of the narrow shape (256 x 18 chunks of 16 bytes = 72 KiB) holds a
+// whole 64-token page of 1152-byte rows, so all of a page's loads are in
+// flight at once; the wide shape (1024 x 5) does the same with four times the
+// waves per workgroup.  Few pages (one wave of workgroups over the chip) run
+// best narrow, many pages wide.
+template <int NT, int U>
+struct Shape {
+  static constexpr int threads = NT;
+  static constexpr int unroll = U;
+  static constexpr int waves = NT / 64;
+};
+using Narrow = Shape<256, 18>;
+using Wide = Shape<1024, 5>;
 
-constexpr int kThreads = PKVG_THREADS;
-constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = PKVG_UNROLL;
 constexpr int kScanThreads = 1024;
 
 // how a page's rows sit in memory
@@ -116,15 +123,26 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t d, uint32_t m
   return q;
 }
 
-// Keeps the compiler from sinking a batch of loads down to their stores (it
-// otherwise interleaves load, wait, store and leaves one load in flight).  The
-// page pointers are deliberately not __restrict__: with them the compiler may
-// move the loads across this fence.
-__device__ __forceinline__ void loads_before_stores() { asm volatile("" ::: "memory"); }
+// Native vector types: they stay in VGPRs through every transformation (the
+// HIP uint4/uint2 wrapper structs can end up in scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Page data is touched exactly once: nontemporal loads and stores (the "nt"
+// cache policy) stream it through the caches without displacing other lines.
+template <typename V>
+__device__ __forceinline__ V load_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+}
+
+template <typename V>
+__device__ __forceinline__ void store_stream(uint8_t* p, V v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+}
 
 template <int BYTES> struct VecOf;
-template <> struct VecOf<16> { using T = uint4; };
-template <> struct VecOf<8> { using T = uint2; };
+template <> struct VecOf<16> { using T = u32x4; };
+template <> struct VecOf<8> { using T = u32x2; };
 template <> struct VecOf<4> { using T = uint32_t; };
 template <> struct VecOf<2> { using T = uint16_t; };
 template <> struct VecOf<1> { using T = uint8_t; };
@@ -182,10 +200,11 @@ struct Page {
 // Fill the LDS task prefix for the fused path: P[0..R] exclusive prefix of page
 // counts, B[0..R] clamped output begins (B[R] = clamped end of the last
 // request), S[0..R) source starts.  Every thread of the workgroup takes part.
+template <int NT>
 __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t* P, int32_t* B,
                                                  int32_t* S, int32_t* scan_tmp) {
   const int32_t R = p.num_reqs;
-  const int32_t per = (R + kThreads - 1) / kThreads;
+  const int32_t per = (R + NT - 1) / NT;
   const int32_t lo = min(static_cast<int32_t>(threadIdx.x) * per, R);
   const int32_t hi = min(lo + per, R);
   int32_t sum = 0;
@@ -200,7 +219,7 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
     sum += c;
   }
   int32_t total;
-  int32_t off = block_exclusive_scan<kThreads>(sum, scan_tmp, total);
+  int32_t off = block_exclusive_scan<NT>(sum, scan_tmp, total);
   for (int32_t r = lo; r < hi; ++r) {
     const int32_t c = P[r];
     P[r] = off;
@@ -211,6 +230,44 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
     B[R] = static_cast<int32_t>(clamp_rows(p.cu_seq_lens[R], p.num_tokens));
   }
   __syncthreads();
+}
+
+// Batches of at most 64 requests: every wave holds the whole task prefix in
+// registers (lane r <-> request r), built without LDS or a barrier.
+constexpr int kWaveMaxReqs = 64;
+
+struct WavePrefix {
+  int32_t incl;   // inclusive prefix of page counts up to this lane's request
+  int32_t count;  // this lane's page count
+  int32_t b;      // clamped output begin of this lane's request
+  int32_t e;      // clamped output end
+  int32_t s;      // source start
+  int32_t total;  // all tasks (uniform)
+};
+
+__device__ __forceinline__ WavePrefix build_prefix_wave(const GatherParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int32_t R = p.num_reqs;
+  WavePrefix w;
+  int32_t cb = 0, ce = 0, st = 0;
+  if (lane < R) {
+    cb = p.cu_seq_lens[lane];
+    ce = p.cu_seq_lens[lane + 1];
+    st = p.seq_starts ? p.seq_starts[lane] : 0;
+  }
+  w.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
+  w.e = static_cast<int32_t>(clamp_rows(ce, p.num_tokens));
+  w.s = st;
+  w.count = lane < R ? page_count(w.b, w.e, w.s, p.block_size) : 0;
+  int32_t incl = w.count;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  w.incl = incl;
+  w.total = uniform(__shfl(incl, 63, 64));
+  return w;
 }
 
 // Largest r in [0, R) with P[r] <= task (P non-decreasing, P[0] = 0).
@@ -268,69 +325,40 @@ __device__ __forceinline__ Page page_from(const GatherParams& p, int64_t phys, i
 // page bodies
 // ---------------------------------------------------------------------------
 
-// Raw copy of `rows` rows.  VW: bytes per lane access.  Every lane issues its
-// kUnroll loads back to back before the first store.  A lane whose chunk index
-// runs past the end works on the last chunk instead: it loads it and stores
-// the same bytes to the same place as that chunk's own lane, so no access
-// needs a branch and all loads stay in flight together.
-template <int VW, int LAYOUT>
-__device__ __forceinline__ void copy_rows_raw(const GatherParams& p, const uint8_t* s, uint8_t* d,
-                                              int32_t rows) {
-  using V = typename VecOf<VW>::T;
-  const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
-  const uint32_t n = static_cast<uint32_t>(rows) * cpr;
-  const uint32_t last = n - 1;
-  for (uint32_t c0 = threadIdx.x; c0 - threadIdx.x < n; c0 += kThreads * kUnroll) {
-    V v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t c = min(c0 + u * kThreads, last);
-      if constexpr (LAYOUT == kFlat) {
-        v[u] = *reinterpret_cast<const V*>(s + c * VW);
-      } else {
-        const uint32_t row = div_magic(c, cpr, p.chunks_magic);
-        const uint32_t col = c - row * cpr;
-        v[u] = *reinterpret_cast<const V*>(s + row * p.src_token_stride + col * VW);
-      }
-    }
-    loads_before_stores();
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t c = min(c0 + u * kThreads, last);
-      if constexpr (LAYOUT == kFlat) {
-        *reinterpret_cast<V*>(d + c * VW) = v[u];
-      } else {
-        const uint32_t row = div_magic(c, cpr, p.chunks_magic);
-        const uint32_t col = c - row * cpr;
-        *reinterpret_cast<V*>(d + row * p.dst_row_stride + col * VW) = v[u];
-      }
-    }
-  }
-}
+// K fp8 codes held in registers: 8 codes in two dwords, fewer in one.
+template <int K> struct CodesOf { using T = uint32_t; };
+template <> struct CodesOf<8> { using T = u32x2; };
 
 // K fp8 codes, read as one K-byte word when SRC_VEC (aligned) else byte by byte.
 template <int K, bool SRC_VEC>
-__device__ __forceinline__ void load_codes(const uint8_t* q, uint32_t (&w)[(K + 3) / 4]) {
+__device__ __forceinline__ typename CodesOf<K>::T load_codes(const uint8_t* q) {
   if constexpr (SRC_VEC && K == 8) {
-    const uint2 x = *reinterpret_cast<const uint2*>(q);
-    w[0] = x.x;
-    w[1] = x.y;
+    return load_stream<u32x2>(q);
   } else if constexpr (SRC_VEC && K == 4) {
-    w[0] = *reinterpret_cast<const uint32_t*>(q);
+    return load_stream<uint32_t>(q);
   } else if constexpr (SRC_VEC && K == 2) {
-    w[0] = *reinterpret_cast<const uint16_t*>(q);
+    return load_stream<uint16_t>(q);
+  } else if constexpr (K == 8) {
+    u32x2 w = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w.x |= static_cast<uint32_t>(q[i]) << (8 * i);
+      w.y |= static_cast<uint32_t>(q[4 + i]) << (8 * i);
+    }
+    return w;
   } else {
+    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < (K + 3) / 4; ++i) w[i] = 0;
-#pragma unroll
-    for (int i = 0; i < K; ++i) w[i / 4] |= static_cast<uint32_t>(q[i]) << (8 * (i % 4));
+    for (int i = 0; i < K; ++i) w |= static_cast<uint32_t>(q[i]) << (8 * i);
+    return w;
   }
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Two codes (bytes 0-1 or 2-3 of w) -> two bf16 packed in one dword.
+// Two codes (bytes 0-1 or 2-3 of w) -> two bf16 packed in one dword:
+// v_cvt_pk_f32_fp8 (exact), v_mul_f32 by the scale, v_cvt_pk_bf16_f32 (RNE).
 __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, bool high, float scale) {
   f32x2 f = high ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
   f.x = f.x * scale;
@@ -345,64 +373,94 @@ struct OutOf {
 };
 
 template <int K>
-__device__ __forceinline__ typename OutOf<K>::T dequant_codes(const uint32_t (&w)[(K + 3) / 4], float scale) {
+__device__ __forceinline__ typename OutOf<K>::T dequant_codes(typename CodesOf<K>::T w, float scale) {
   if constexpr (K == 8) {
-    uint4 o;
-    o.x = dequant_pair(w[0], false, scale);
-    o.y = dequant_pair(w[0], true, scale);
-    o.z = dequant_pair(w[1], false, scale);
-    o.w = dequant_pair(w[1], true, scale);
+    u32x4 o;
+    o.x = dequant_pair(w.x, false, scale);
+    o.y = dequant_pair(w.x, true, scale);
+    o.z = dequant_pair(w.y, false, scale);
+    o.w = dequant_pair(w.y, true, scale);
     return o;
   } else if constexpr (K == 4) {
-    uint2 o;
-    o.x = dequant_pair(w[0], false, scale);
-    o.y = dequant_pair(w[0], true, scale);
+    u32x2 o;
+    o.x = dequant_pair(w, false, scale);
+    o.y = dequant_pair(w, true, scale);
     return o;
   } else if constexpr (K == 2) {
-    return dequant_pair(w[0], false, scale);
+    return dequant_pair(w, false, scale);
   } else {
-    return static_cast<uint16_t>(dequant_pair(w[0], false, scale) & 0xFFFFu);
+    return static_cast<uint16_t>(dequant_pair(w, false, scale) & 0xFFFFu);
   }
 }
 
-// fp8 -> bf16 of `rows` rows; K codes per lane access.  Chunk indices are
-// clamped to the last chunk as in copy_rows_raw (a clamped lane writes the
-// same bf16 values as the chunk's own lane), so all loads are in flight
-// together.
-template <int K, int LAYOUT, bool SRC_VEC>
-__device__ __forceinline__ void copy_rows_fp8(const GatherParams& p, const uint8_t* s, uint8_t* d,
-                                              int32_t rows, float scale) {
-  using O = typename OutOf<K>::T;
-  constexpr int NW = (K + 3) / 4;
-  const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
-  const uint32_t n = static_cast<uint32_t>(rows) * cpr;
-  const uint32_t last = n - 1;
-  for (uint32_t c0 = threadIdx.x; c0 - threadIdx.x < n; c0 += kThreads * kUnroll) {
-    uint32_t w[kUnroll][NW];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t c = min(c0 + u * kThreads, last);
-      if constexpr (LAYOUT == kFlat) {
-        load_codes<K, SRC_VEC>(s + c * K, w[u]);
-      } else {
-        const uint32_t row = div_magic(c, cpr, p.chunks_magic);
-        const uint32_t col = c - row * cpr;
-        load_codes<K, SRC_VEC>(s + row * p.src_token_stride + col * K, w[u]);
-      }
+// How one chunk of a page moves: a raw chunk is W bytes; an fp8 chunk is W
+// codes in, 2W bytes of bf16 out.  Chunk c of a page lies at byte c * in_bytes
+// (kFlat) or at row c / chunks_per_row, column c % chunks_per_row (kRows).
+template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+struct Mover {
+  static constexpr int in_bytes = W;
+  static constexpr int out_bytes = CONVERT == kCopy ? W : 2 * W;
+  using Reg = typename std::conditional<CONVERT == kCopy, typename VecOf<W>::T, typename CodesOf<W>::T>::type;
+
+  __device__ static __forceinline__ void load(const GatherParams& p, const uint8_t* s, uint32_t c, Reg& r) {
+    const uint8_t* q;
+    if constexpr (LAYOUT == kFlat) {
+      q = s + c * in_bytes;
+    } else {
+      const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
+      const uint32_t row = div_magic(c, cpr, p.chunks_magic);
+      q = s + row * p.src_token_stride + (c - row * cpr) * in_bytes;
     }
-    loads_before_stores();
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t c = min(c0 + u * kThreads, last);
-      const O o = dequant_codes<K>(w[u], scale);
-      if constexpr (LAYOUT == kFlat) {
-        *reinterpret_cast<O*>(d + c * (2 * K)) = o;
-      } else {
-        const uint32_t row = div_magic(c, cpr, p.chunks_magic);
-        const uint32_t col = c - row * cpr;
-        *reinterpret_cast<O*>(d + row * p.dst_row_stride + col * (2 * K)) = o;
-      }
+    if constexpr (CONVERT == kCopy) r = load_stream<Reg>(q);
+    else r = load_codes<W, SRC_VEC>(q);
+  }
+
+  __device__ static __forceinline__ void store(const GatherParams& p, uint8_t* d, uint32_t c, const Reg& r,
+                                               float scale) {
+    uint8_t* q;
+    if constexpr (LAYOUT == kFlat) {
+      q = d + c * out_bytes;
+    } else {
+      const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
+      const uint32_t row = div_magic(c, cpr, p.chunks_magic);
+      q = d + row * p.dst_row_stride + (c - row * cpr) * out_bytes;
     }
+    if constexpr (CONVERT == kCopy) store_stream(q, r);
+    else store_stream(q, dequant_codes<W>(r, scale));
+  }
+};
+
+// A batch is SH::unroll chunks per lane: chunks c0 + u * SH::threads.  Every
+// lane issues its loads back to back; a lane whose chunk runs past the end
+// (n chunks) loads the last chunk again (in bounds, one cache line) and later
+// skips its store, so the loads carry no branch.  The page pointers are
+// deliberately not __restrict__: that keeps the compiler from moving a load
+// below an earlier store (which would interleave load, wait, store).
+template <class SH, class M>
+__device__ __forceinline__ void load_batch(const GatherParams& p, const uint8_t* s, uint32_t n, uint32_t c0,
+                                           typename M::Reg (&r)[SH::unroll]) {
+#pragma unroll
+  for (int u = 0; u < SH::unroll; ++u) M::load(p, s, min(c0 + u * SH::threads, n - 1), r[u]);
+}
+
+template <class SH, class M>
+__device__ __forceinline__ void store_batch(const GatherParams& p, uint8_t* d, uint32_t n, uint32_t c0,
+                                            const typename M::Reg (&r)[SH::unroll], float scale) {
+#pragma unroll
+  for (int u = 0; u < SH::unroll; ++u) {
+    const uint32_t c = c0 + u * SH::threads;
+    if (c < n) M::store(p, d, c, r[u], scale);
+  }
+}
+
+// A page of any size: batch after batch.
+template <class SH, class M>
+__device__ __forceinline__ void move_page(const GatherParams& p, const uint8_t* s, uint8_t* d, uint32_t n,
+                                          float scale) {
+  for (uint32_t c0 = threadIdx.x; c0 - threadIdx.x < n; c0 += SH::threads * SH::unroll) {
+    typename M::Reg r[SH::unroll];
+    load_batch<SH, M>(p, s, n, c0, r);
+    store_batch<SH, M>(p, d, n, c0, r, scale);
   }
 }
 
@@ -410,55 +468,105 @@ __device__ __forceinline__ void copy_rows_fp8(const GatherParams& p, const uint8
 // the gather kernel
 // ---------------------------------------------------------------------------
 
-// CONVERT == kCopy: W = bytes per lane access.  CONVERT == kFp8Bf16: W = codes
-// per lane access.  Grid: any size; workgroup w takes tasks w, w + gridDim.x, ...
-// Dynamic LDS (fused path): (3 * num_reqs + 2) int32.
-template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
-__global__ __launch_bounds__(kThreads) void gather_pages_kernel(GatherParams p) {
-  extern __shared__ int32_t lds[];
-  __shared__ int32_t scan_tmp[kWaves];
+// Task lookup for one workgroup: in-wave registers (small batches), an LDS
+// prefix, a prebuilt task table (large batches), or one request.
+enum TaskMode : int { kWaveRegs = 0, kLdsPrefix = 1, kTable = 2, kSingle = 3 };
 
-  const bool fused = p.tasks == nullptr;
+struct TaskSource {
+  int mode;
+  WavePrefix wp;
+  const int32_t* P;
+  const int32_t* B;
+  const int32_t* S;
+  int32_t b, e, s;         // kSingle: the request's clamped extent and source start
+  int32_t first_phys_raw;  // kSingle: block-table entry of this workgroup's first task (raw)
+};
+
+// Resolve `task` (the same for every lane) to its page, all fields wave-uniform.
+__device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSource& ts, int32_t task) {
+  if (ts.mode == kSingle) {
+    const TaskGeom g = task_geometry(task, ts.b, ts.e, ts.s, p.block_size);
+    int64_t phys;
+    if (task == static_cast<int32_t>(blockIdx.x)) {
+      phys = g.logical < p.block_table_width ? ts.first_phys_raw : -1;
+      if (phys >= p.num_blocks) phys = -1;
+    } else {
+      phys = lookup_block(p, 0, g.logical);
+    }
+    return page_from(p, uniform64(phys < 0 ? -1 : phys), g.pbeg, g.pend, g.out_begin);
+  }
+  if (ts.mode == kWaveRegs) {
+    // the task's request: the number of requests whose inclusive prefix is <= task
+    const int32_t r = uniform(static_cast<int32_t>(__popcll(__ballot(ts.wp.incl <= task))));
+    const int32_t b = uniform(__builtin_amdgcn_readlane(ts.wp.b, r));
+    const int32_t e = uniform(__builtin_amdgcn_readlane(ts.wp.e, r));
+    const int32_t s = uniform(__builtin_amdgcn_readlane(ts.wp.s, r));
+    const int32_t first = uniform(__builtin_amdgcn_readlane(ts.wp.incl - ts.wp.count, r));
+    const TaskGeom g = task_geometry(task - first, b, e, s, p.block_size);
+    return page_from(p, uniform64(lookup_block(p, r, g.logical)), g.pbeg, g.pend, g.out_begin);
+  }
+  if (ts.mode == kLdsPrefix) {
+    const int32_t r = uniform(find_request(ts.P, p.num_reqs, task));
+    const TaskGeom g = task_geometry(task - uniform(ts.P[r]), uniform(ts.B[r]), uniform(ts.B[r + 1]),
+                                     uniform(ts.S[r]), p.block_size);
+    return page_from(p, uniform64(lookup_block(p, r, g.logical)), g.pbeg, g.pend, g.out_begin);
+  }
+  const TaskRecord t = p.tasks[task];
+  return page_from(p, uniform(t.phys), uniform(t.page_begin), uniform(t.page_end),
+                   static_cast<int64_t>(uniform(t.out_begin)));
+}
+
+// CONVERT == kCopy: W = bytes per lane access.  CONVERT == kFp8Bf16: W = codes
+// per lane access.  Grid: any size (the host launches one workgroup per task);
+// workgroup w takes tasks w, w + gridDim.x, ...  Dynamic LDS (LDS-prefix mode,
+// 64 < num_reqs): (3 * num_reqs + 2) int32.
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+__global__ __launch_bounds__(SH::threads) void gather_pages_kernel(GatherParams p) {
+  using M = Mover<CONVERT, W, LAYOUT, SRC_VEC>;
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t scan_tmp[SH::waves];
+
   const int32_t R = p.num_reqs;
+  TaskSource ts;
+  ts.mode = p.tasks != nullptr ? kTable : (R == 1 ? kSingle : (R <= kWaveMaxReqs ? kWaveRegs : kLdsPrefix));
   int32_t* P = lds;
   int32_t* B = lds + (R + 1);
   int32_t* S = lds + 2 * (R + 1);
+  ts.P = P;
+  ts.B = B;
+  ts.S = S;
   float scale = 1.0f;
   if constexpr (CONVERT == kFp8Bf16)
     scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*p.scale)));
 
   int32_t num_tasks;
-  if (fused) {
-    build_prefix_lds(p, P, B, S, scan_tmp);
+  if (ts.mode == kSingle) {
+    // The first page's logical block is seq_start / block_size + blockIdx.x:
+    // its block-table entry is requested together with the request extent
+    // instead of after it (one dependent memory round trip less).
+    ts.s = p.seq_starts ? uniform(p.seq_starts[0]) : 0;
+    const int64_t lb0 = ts.s / p.block_size + blockIdx.x;
+    ts.first_phys_raw = lb0 < p.block_table_width ? uniform(p.block_table[lb0]) : -1;
+    ts.b = static_cast<int32_t>(clamp_rows(uniform(p.cu_seq_lens[0]), p.num_tokens));
+    ts.e = static_cast<int32_t>(clamp_rows(uniform(p.cu_seq_lens[1]), p.num_tokens));
+    num_tasks = page_count(ts.b, ts.e, ts.s, p.block_size);
+  } else if (ts.mode == kWaveRegs) {
+    ts.wp = build_prefix_wave(p);
+    num_tasks = ts.wp.total;
+  } else if (ts.mode == kLdsPrefix) {
+    build_prefix_lds<SH::threads>(p, P, B, S, scan_tmp);
     num_tasks = P[R];
   } else {
     num_tasks = min(*p.task_count, p.task_capacity);
   }
   num_tasks = uniform(num_tasks);
 
+  const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
   for (int32_t task = blockIdx.x; task < num_tasks; task += gridDim.x) {
-    Page pg;
-    if (fused) {
-      const int32_t r = uniform(find_request(P, R, task));
-      const int64_t b = uniform(B[r]);
-      const int64_t e = uniform(B[r + 1]);
-      const int64_t s = uniform(S[r]);
-      const TaskGeom g = task_geometry(task - uniform(P[r]), b, e, s, p.block_size);
-      const int64_t phys = uniform64(lookup_block(p, r, g.logical));
-      pg = page_from(p, phys, g.pbeg, g.pend, g.out_begin);
-    } else {
-      const TaskRecord t = p.tasks[task];
-      pg = page_from(p, uniform(t.phys), uniform(t.page_begin), uniform(t.page_end),
-                     static_cast<int64_t>(uniform(t.out_begin)));
-    }
+    const Page pg = resolve_task(p, ts, task);
     if (pg.rows <= 0) continue;
-    const uint8_t* s = p.src + uniform64(pg.src_off);
-    uint8_t* d = p.dst + uniform64(pg.dst_off);
-    if constexpr (CONVERT == kCopy) {
-      copy_rows_raw<W, LAYOUT>(p, s, d, pg.rows);
-    } else {
-      copy_rows_fp8<W, LAYOUT, SRC_VEC>(p, s, d, pg.rows, scale);
-    }
+    move_page<SH, M>(p, p.src + uniform64(pg.src_off), p.dst + uniform64(pg.dst_off),
+                     static_cast<uint32_t>(pg.rows) * cpr, scale);
   }
 }
 

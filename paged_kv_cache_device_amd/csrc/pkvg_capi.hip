@@ -17,9 +17,12 @@ using pkvg::TaskRecord;
 
 thread_local int g_last_hip_error = 0;
 
-// Workgroups launched for the fused path: one per task (up to this cap); any
-// grid is correct because workgroups stride over tasks.
-constexpr int64_t kMaxGrid = int64_t(1) << 20;
+// Workgroups launched: one per task up to this cap; any grid is correct
+// because workgroups stride over tasks.
+#ifndef PKVG_MAX_GRID
+#define PKVG_MAX_GRID (1 << 20)
+#endif
+constexpr int64_t kMaxGrid = PKVG_MAX_GRID;
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -71,10 +74,19 @@ int64_t max_bytes_stride(int64_t stride, int64_t elem) {
   return stride > INT64_MAX / elem ? -1 : stride * elem;
 }
 
+// Launches with at least this many page tasks (about four workgroups per CU)
+// use the wide workgroup shape; fewer use the narrow one.
+constexpr int64_t kWideMinTasks = 1024;
+
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((pkvg::gather_pages_kernel<CONVERT, W, LAYOUT, SRC_VEC>), dim3(grid),
-                     dim3(pkvg::kThreads), lds, stream, p);
+  if (grid >= kWideMinTasks) {
+    hipLaunchKernelGGL((pkvg::gather_pages_kernel<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>), dim3(grid),
+                       dim3(pkvg::Wide::threads), lds, stream, p);
+  } else {
+    hipLaunchKernelGGL((pkvg::gather_pages_kernel<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>), dim3(grid),
+                       dim3(pkvg::Narrow::threads), lds, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -128,7 +140,7 @@ int run_plan(Plan& pl, hipStream_t stream) {
   const int32_t R = pl.p.num_reqs;
   if (R <= PKVG_FUSED_MAX_REQS) {
     const int64_t g = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
-    const size_t lds = sizeof(int32_t) * (3 * size_t(R) + 3);
+    const size_t lds = R <= pkvg::kWaveMaxReqs ? 0 : sizeof(int32_t) * (3 * size_t(R) + 3);
     hipError_t e = dispatch(pl, static_cast<unsigned>(g), lds, stream);
     return e == hipSuccess ? PKVG_OK : hip_fail(e);
   }

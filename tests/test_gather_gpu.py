@@ -256,3 +256,30 @@ def test_offsets_beyond_2_to_31_bytes():
     rows = o.gather_tensors(oracle.MODE_COPY, cache.cpu(), want[:T], bt, cu, None, 1)
     assert rows == T
     assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# one request: the path that requests the first block-table entry early
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tokens,start,bs,kind", [
+    (61440, 0, 64, workloads.RAW),            # narrow shape, whole pages
+    (5000, 37, 16, workloads.RAW),            # partial first and last pages
+    (130000, 1000, 64, workloads.UPCONVERT),  # wide shape (>= 1024 pages)
+    (70000, 63, 64, workloads.DEQUANT_FP8),
+])
+def test_single_request(tokens, start, bs, kind):
+    wl = workloads.make_workload(f"single_{tokens}_{start}", kind, [tokens], bs, 576,
+                                 -(-tokens // bs) + 9, seed=tokens, starts=[start], scale=0.05)
+    check_parity(wl, DEV)
+    # guards on the single-request path: a hole in the table, an id past the
+    # cache, and a table narrower than the request
+    bt = wl.block_table
+    bt[0, 1] = -1
+    bt[0, 2] = wl.num_blocks + 3
+    wl.block_table = bt[:, : bt.shape[1] - 2].contiguous()
+    check_parity(wl, DEV)
+    # fewer destination rows than the request's extent
+    wl.num_tokens = tokens // 3
+    wl.workspace = wl.workspace[: tokens // 3 + 5].clone()
+    check_parity(wl, DEV)
