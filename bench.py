@@ -58,6 +58,43 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def summarize_counters(prof_dir: str, workload: str, calib_mib: int, command: str) -> dict:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; files
+    fetch_counter_collection.csv and write_counter_collection.csv in prof_dir)
+    into HBM bytes per gather launch.  Each counter is scaled by what it reads
+    for the plain device copies of `calib_mib` MiB that the run ends with (the
+    last 10 copy-kernel dispatches), and the result is written to
+    profiles/traffic_<workload>.json together with the kernel-source hash."""
+    import csv
+
+    import workloads
+
+    def rows(kind):
+        with open(os.path.join(prof_dir, f"{kind}_counter_collection.csv")) as f:
+            return sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+
+    out = {}
+    for kind, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        rs = [r for r in rows(kind) if r["Counter_Name"] == counter]
+        gather = [float(r["Counter_Value"]) for r in rs if "gather_pages_kernel" in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]][-10:]
+        known = calib_mib << 20
+        factor = known / (statistics.median(copies) * 1024.0)
+        out[kind] = {"counter": counter, "gather_kib_median": statistics.median(gather),
+                     "launches": len(gather), "calibration_kib_median": statistics.median(copies),
+                     "calibration_bytes": known, "scale": round(factor, 5),
+                     "bytes_per_launch": statistics.median(gather) * 1024.0 * factor}
+    wl = workloads.named(workload)
+    total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    res = {"workload": workload, "kernel_source_sha": kernel_source_hash(),
+           "hbm_bytes_per_launch": round(total), "algorithmic_bytes": wl.algorithmic_bytes(),
+           "traffic_over_algorithmic": round(total / wl.algorithmic_bytes(), 5),
+           "fetch": out["fetch"], "write": out["write"], "command": command}
+    with open(os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
 def call_for(wl, ws):
     """The library call for workload ``wl`` into workspace ``ws``, marshalled once."""
     import paged_kv_cache_device_amd as pkvg
@@ -189,9 +226,23 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--only-gather", action="store_true",
                     help="run warmup + steps of the gather and nothing else (for profilers)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="with --only-gather: then run 10 device copies of this many MiB "
+                         "(a plain copy kernel of known size, to scale traffic counters)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--summarize-counters", metavar="PROF_DIR",
+                    help="summarize rocprofv3 FETCH_SIZE/WRITE_SIZE runs of --workload into "
+                         "profiles/traffic_<workload>.json and exit (no GPU needed)")
+    ap.add_argument("--counter-command", default="",
+                    help="with --summarize-counters: the profiling command, stored verbatim")
     ap.add_argument("--cold-reps", type=int, default=100)
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        res = summarize_counters(args.summarize_counters, args.workload, args.calibration_copy_mib,
+                                 args.counter_command)
+        print(json.dumps(res, indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the gather "
@@ -216,6 +267,15 @@ def main():
     if args.only_gather:
         wall, _ = time_steps(sets, args.steps, args.warmup)
         log(f"[bench] only-gather: {args.steps} steps in {wall * 1e3:.2f} ms")
+        if args.calibration_copy_mib:
+            n = args.calibration_copy_mib << 20
+            bufs = [(torch.empty(n, dtype=torch.uint8, device=dev),
+                      torch.empty(n, dtype=torch.uint8, device=dev)) for _ in range(4)]
+            for i in range(10):
+                s_, d_ = bufs[i % 4]
+                d_.copy_(s_)
+            torch.cuda.synchronize()
+            log(f"[bench] calibration: 10 copies of {n} bytes")
         return
 
     # the timed region: exactly `steps` calls; HIP events on the launch stream
