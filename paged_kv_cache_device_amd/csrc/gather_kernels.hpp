@@ -36,20 +36,21 @@
 
 namespace pkvg {
 
-// Workgroup shapes: threads per workgroup and chunks per lane per batch.  A
-// batch of the narrow shape (256 x 18 chunks of 16 bytes = 72 KiB) holds a
-// whole 64-token page of 1152-byte rows, so all of a page's loads are in
-// flight at once; the wide shape (1024 x 5) does the same with four times the
+// Workgroup shapes: threads per workgroup and output bytes per lane per batch.
+// A narrow batch (256 lanes x 288 bytes = 72 KiB of output) holds a whole
+// 64-token page of 1152-byte rows, so all of a page's loads are in flight at
+// once; the wide shape (1024 x 80 bytes) does the same with four times the
 // waves per workgroup.  Few pages (one wave of workgroups over the chip) run
-// best narrow, many pages wide.
-template <int NT, int U>
+// best narrow, many pages wide.  Chunks per lane per batch follow from the
+// chunk's output size (see unroll_of).
+template <int NT, int LANE_BYTES>
 struct Shape {
   static constexpr int threads = NT;
-  static constexpr int unroll = U;
+  static constexpr int lane_bytes = LANE_BYTES;
   static constexpr int waves = NT / 64;
 };
-using Narrow = Shape<256, 18>;
-using Wide = Shape<1024, 5>;
+using Narrow = Shape<256, 288>;
+using Wide = Shape<1024, 80>;
 
 constexpr int kScanThreads = 1024;
 
@@ -97,6 +98,7 @@ struct GatherParams {
   int32_t block_size;
   int32_t block_table_width;
   int32_t chunks_per_row;        // row chunks (kRows), or chunks per row of the flat span (kFlat)
+  int32_t row_in_bytes;          // bytes of a source row that are gathered
   uint32_t chunks_magic;         // ceil(2^32 / chunks_per_row), or 0xFFFFFFFF for 1
   int32_t task_capacity;         // with tasks: records available
 };
@@ -393,6 +395,53 @@ __device__ __forceinline__ typename OutOf<K>::T dequant_codes(typename CodesOf<K
   }
 }
 
+// Where a page's source rows are read from.  fp8 code rows that are not
+// K-aligned (a 577-byte row pitch, say) are read as dword-aligned windows
+// around each lane's K codes, then shifted into place: one 12- or 8-byte load
+// instead of K byte loads.  A window is clamped to end at `lim`, the page's
+// used bytes rounded up to a whole dword, so no load touches a dword that
+// holds none of the page's codes.
+struct PageSrc {
+  const uint8_t* ptr;    // first copied row of the page
+  const uint8_t* base4;  // windowed mode: ptr rounded down to 4 bytes
+  uint32_t delta;        // windowed mode: ptr - base4
+  uint32_t lim;          // windowed mode: used bytes from base4, rounded up to 4
+};
+
+__device__ __forceinline__ PageSrc page_src(const uint8_t* ptr, uint32_t used_bytes) {
+  PageSrc ps;
+  ps.ptr = ptr;
+  ps.delta = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ptr) & 3u);
+  ps.base4 = ptr - ps.delta;
+  ps.lim = (used_bytes + ps.delta + 3u) & ~3u;
+  return ps;
+}
+
+// K (4 or 8) codes at byte `off` from base4, any alignment.  The window starts
+// at the dword holding byte `off`, or earlier when that would pass `lim`; the
+// codes then sit 0..4 bytes into it.  Needs lim >= 12 (K = 8) or 8 (K = 4).
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+template <int K>
+__device__ __forceinline__ typename CodesOf<K>::T load_codes_window(const uint8_t* base4, uint32_t off,
+                                                                   uint32_t lim) {
+  constexpr uint32_t kWin = K == 8 ? 12u : 8u;
+  const uint32_t a = min(off & ~3u, lim - kWin);
+  const uint32_t sh = off - a;
+  if constexpr (K == 8) {
+    const u32x2_a4 lo = load_stream<u32x2_a4>(base4 + a);
+    const uint32_t hi = load_stream<uint32_t>(base4 + a + 8);
+    u32x2 w;
+    w.x = sh == 4 ? lo.y : __builtin_amdgcn_alignbyte(lo.y, lo.x, sh);
+    w.y = sh == 4 ? hi : __builtin_amdgcn_alignbyte(hi, lo.y, sh);
+    return w;
+  } else {
+    static_assert(K == 4, "windowed code loads take 4 or 8 codes");
+    const u32x2_a4 d = load_stream<u32x2_a4>(base4 + a);
+    return sh == 4 ? d.y : __builtin_amdgcn_alignbyte(d.y, d.x, sh);
+  }
+}
+
 // How one chunk of a page moves: a raw chunk is W bytes; an fp8 chunk is W
 // codes in, 2W bytes of bf16 out.  Chunk c of a page lies at byte c * in_bytes
 // (kFlat) or at row c / chunks_per_row, column c % chunks_per_row (kRows).
@@ -400,19 +449,22 @@ template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 struct Mover {
   static constexpr int in_bytes = W;
   static constexpr int out_bytes = CONVERT == kCopy ? W : 2 * W;
+  // unaligned fp8 code rows of 4 or 8 codes per lane are read as shifted windows
+  static constexpr bool windowed = CONVERT == kFp8Bf16 && !SRC_VEC && (W == 4 || W == 8);
   using Reg = typename std::conditional<CONVERT == kCopy, typename VecOf<W>::T, typename CodesOf<W>::T>::type;
 
-  __device__ static __forceinline__ void load(const GatherParams& p, const uint8_t* s, uint32_t c, Reg& r) {
-    const uint8_t* q;
+  __device__ static __forceinline__ void load(const GatherParams& p, const PageSrc& src, uint32_t c, Reg& r) {
+    uint32_t off;  // byte offset of chunk c from the page's first row
     if constexpr (LAYOUT == kFlat) {
-      q = s + c * in_bytes;
+      off = c * in_bytes;
     } else {
       const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
       const uint32_t row = div_magic(c, cpr, p.chunks_magic);
-      q = s + row * p.src_token_stride + (c - row * cpr) * in_bytes;
+      off = row * static_cast<uint32_t>(p.src_token_stride) + (c - row * cpr) * in_bytes;
     }
-    if constexpr (CONVERT == kCopy) r = load_stream<Reg>(q);
-    else r = load_codes<W, SRC_VEC>(q);
+    if constexpr (windowed) r = load_codes_window<W>(src.base4, off + src.delta, src.lim);
+    else if constexpr (CONVERT == kCopy) r = load_stream<Reg>(src.ptr + off);
+    else r = load_codes<W, SRC_VEC>(src.ptr + off);
   }
 
   __device__ static __forceinline__ void store(const GatherParams& p, uint8_t* d, uint32_t c, const Reg& r,
@@ -430,24 +482,32 @@ struct Mover {
   }
 };
 
-// A batch is SH::unroll chunks per lane: chunks c0 + u * SH::threads.  Every
+// Chunks per lane per batch: the shape's output bytes per lane over one
+// chunk's output bytes, at most 18 (16-byte chunks: 18 narrow, 5 wide).
+template <class SH, class M>
+constexpr int unroll_of() {
+  constexpr int u = SH::lane_bytes / M::out_bytes;
+  return u < 1 ? 1 : (u > 18 ? 18 : u);
+}
+
+// A batch is U = unroll_of<SH, M>() chunks per lane: chunks c0 + u * SH::threads.  Every
 // lane issues its loads back to back; a lane whose chunk runs past the end
 // (n chunks) loads the last chunk again (in bounds, one cache line) and later
 // skips its store, so the loads carry no branch.  The page pointers are
 // deliberately not __restrict__: that keeps the compiler from moving a load
 // below an earlier store (which would interleave load, wait, store).
 template <class SH, class M>
-__device__ __forceinline__ void load_batch(const GatherParams& p, const uint8_t* s, uint32_t n, uint32_t c0,
-                                           typename M::Reg (&r)[SH::unroll]) {
+__device__ __forceinline__ void load_batch(const GatherParams& p, const PageSrc& s, uint32_t n, uint32_t c0,
+                                           typename M::Reg (&r)[unroll_of<SH, M>()]) {
 #pragma unroll
-  for (int u = 0; u < SH::unroll; ++u) M::load(p, s, min(c0 + u * SH::threads, n - 1), r[u]);
+  for (int u = 0; u < unroll_of<SH, M>(); ++u) M::load(p, s, min(c0 + u * SH::threads, n - 1), r[u]);
 }
 
 template <class SH, class M>
 __device__ __forceinline__ void store_batch(const GatherParams& p, uint8_t* d, uint32_t n, uint32_t c0,
-                                            const typename M::Reg (&r)[SH::unroll], float scale) {
+                                            const typename M::Reg (&r)[unroll_of<SH, M>()], float scale) {
 #pragma unroll
-  for (int u = 0; u < SH::unroll; ++u) {
+  for (int u = 0; u < unroll_of<SH, M>(); ++u) {
     const uint32_t c = c0 + u * SH::threads;
     if (c < n) M::store(p, d, c, r[u], scale);
   }
@@ -455,10 +515,11 @@ __device__ __forceinline__ void store_batch(const GatherParams& p, uint8_t* d, u
 
 // A page of any size: batch after batch.
 template <class SH, class M>
-__device__ __forceinline__ void move_page(const GatherParams& p, const uint8_t* s, uint8_t* d, uint32_t n,
+__device__ __forceinline__ void move_page(const GatherParams& p, const PageSrc& s, uint8_t* d, uint32_t n,
                                           float scale) {
-  for (uint32_t c0 = threadIdx.x; c0 - threadIdx.x < n; c0 += SH::threads * SH::unroll) {
-    typename M::Reg r[SH::unroll];
+  constexpr int U = unroll_of<SH, M>();
+  for (uint32_t c0 = threadIdx.x; c0 - threadIdx.x < n; c0 += SH::threads * U) {
+    typename M::Reg r[U];
     load_batch<SH, M>(p, s, n, c0, r);
     store_batch<SH, M>(p, d, n, c0, r, scale);
   }
@@ -565,7 +626,9 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(GatherParams 
   for (int32_t task = blockIdx.x; task < num_tasks; task += gridDim.x) {
     const Page pg = resolve_task(p, ts, task);
     if (pg.rows <= 0) continue;
-    move_page<SH, M>(p, p.src + uniform64(pg.src_off), p.dst + uniform64(pg.dst_off),
+    const uint32_t used = static_cast<uint32_t>(pg.rows - 1) * static_cast<uint32_t>(p.src_token_stride) +
+                          static_cast<uint32_t>(p.row_in_bytes);
+    move_page<SH, M>(p, page_src(p.src + uniform64(pg.src_off), used), p.dst + uniform64(pg.dst_off),
                      static_cast<uint32_t>(pg.rows) * cpr, scale);
   }
 }

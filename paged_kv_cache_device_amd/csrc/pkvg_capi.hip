@@ -193,7 +193,9 @@ int plan_copy(Plan& pl, const void* src, void* dst, int64_t elem, int32_t entry,
   const int64_t sb = max_bytes_stride(sbs, elem), st = max_bytes_stride(sts, elem),
                 dr = max_bytes_stride(drs, elem);
   if (sb < 0 || st < 0 || dr < 0) return PKVG_E_LIMIT;
+  // in-page offsets are 32-bit: a page's source and destination rows span < 2^31 bytes
   if (int64_t(block_size) * row >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  if (int64_t(block_size - 1) * st + row >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
   int w = 16;
   while (w > 1 && (row % w || sb % w || st % w || dr % w || !aligned(src, w) || !aligned(dst, w))) w >>= 1;
   pl.convert = pkvg::kCopy;
@@ -204,6 +206,7 @@ int plan_copy(Plan& pl, const void* src, void* dst, int64_t elem, int32_t entry,
   pl.p.dst_row_stride = dr;
   pl.p.chunks_per_row = static_cast<int32_t>(row / w);
   pl.p.chunks_magic = magic_for(static_cast<uint32_t>(row / w));
+  pl.p.row_in_bytes = static_cast<int32_t>(row);
   return PKVG_OK;
 }
 
@@ -217,14 +220,21 @@ int plan_fp8(Plan& pl, const void* src, void* dst, int32_t entry, int64_t sbs, i
   int k = 8;
   while (k > 1 && (entry % k || dr % (2 * k) || !aligned(dst, 2 * k))) k >>= 1;
   pl.convert = pkvg::kFp8Bf16;
-  pl.width = k;
   pl.src_vec = (sbs % k == 0) && (sts % k == 0) && aligned(src, k);
+  // unaligned code rows are read as shifted dword windows, which need rows of
+  // at least 16 codes; shorter unaligned rows use one code per lane
+  if (!pl.src_vec && k >= 4 && entry < 16) k = 1;
+  pl.width = k;
   pl.layout = (sts == entry && dr == 2 * int64_t(entry)) ? pkvg::kFlat : pkvg::kRows;
   pl.p.src_block_stride = sbs;
   pl.p.src_token_stride = sts;
   pl.p.dst_row_stride = dr;
   pl.p.chunks_per_row = entry / k;
   pl.p.chunks_magic = magic_for(static_cast<uint32_t>(entry / k));
+  pl.p.row_in_bytes = entry;
+  // in-page source offsets are 32-bit (the unaligned path also reads up to 3
+  // bytes around a chunk)
+  if (int64_t(block_size - 1) * sts + entry + 8 >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
   return PKVG_OK;
 }
 
