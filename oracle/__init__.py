@@ -167,13 +167,13 @@ def load() -> Oracle:
     return _default
 
 
-def run_workload(wl, dst=None) -> int:
-    """Oracle gather for a ``workloads.Workload`` on CPU, into ``dst`` (default: a fresh
-    sentinel workspace's dst view).  Returns (workspace, rows written)."""
+def run_workload(wl, ws=None):
+    """Oracle gather for a ``workloads.Workload`` on CPU into the workspace ``ws``
+    (default: a fresh sentinel-filled one).  Returns (workspace, rows written)."""
     import workloads
 
     o = load()
-    ws = wl.fresh_workspace() if dst is None else dst
+    ws = wl.fresh_workspace() if ws is None else ws
     dst_view = ws[: wl.num_tokens, : wl.entry]
     mode = MODE_E4M3FN_TO_BF16 if wl.kind in workloads.FP8_KINDS else MODE_COPY
     rows = o.gather_tensors(mode, wl.src_cache(), dst_view, wl.block_table, wl.cu_seq_lens,

@@ -283,3 +283,56 @@ def test_single_request(tokens, start, bs, kind):
     wl.num_tokens = tokens // 3
     wl.workspace = wl.workspace[: tokens // 3 + 5].clone()
     check_parity(wl, DEV)
+
+
+# ---------------------------------------------------------------------------
+# capture in a HIP graph: every replay recomputes from the current inputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,R", [(workloads.RAW, 1), (workloads.UPCONVERT, 5),
+                                    (workloads.DEQUANT_FP8, 100)])
+def test_graph_replays(kind, R):
+    """The calls enqueue only kernel launches (no memset, no allocation up to
+    1024 requests), so they can be captured.  Between replays the cache
+    contents change and eager work runs; each replay must match the oracle on
+    the inputs of that moment."""
+    import paged_kv_cache_device_amd as pkvg
+
+    g = torch.Generator("cpu").manual_seed(R)
+    lens = torch.randint(1, 300, (R,), generator=g).tolist()
+    starts = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in lens]
+    wl = workloads.make_workload(f"graph_{kind}_{R}", kind, lens, 16, 64,
+                                 sum(-(-n // 16) for n in lens) + 2, seed=R, starts=starts,
+                                 scale=0.05, workspace_rows=sum(lens) + 4)
+    d = wl.to(DEV)
+    ws = d.fresh_workspace()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            if kind == workloads.RAW:
+                pkvg.gather_cache(d.src_cache(), ws[: d.num_tokens, : d.entry], d.block_table,
+                                  d.cu_seq_lens, R, d.seq_starts)
+            elif kind == workloads.UPCONVERT:
+                pkvg.gather_upconvert_fp8(d.src_cache(), ws[: d.num_tokens, : d.entry],
+                                          d.block_table, d.cu_seq_lens, R, d.scale_tensor,
+                                          d.seq_starts)
+            else:
+                pkvg.gather_maybe_dequant(d.src_cache(), ws[: d.num_tokens, : d.entry],
+                                          d.block_table, d.cu_seq_lens, R, "fp8", d.scale_tensor,
+                                          d.seq_starts)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        log(f"[graph] {kind} R={R} replay {rep}")
+        # new cache contents in place (the graph holds the same pointers)
+        fresh = workloads.make_workload("tmp", kind, lens, 16, 64, wl.num_blocks, seed=100 + rep,
+                                        starts=starts, scale=0.05)
+        wl.cache_base.copy_(fresh.cache_base)
+        d.cache_base.copy_(fresh.cache_base)
+        ws.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        _ = (d.cache_base.float().sum() if d.cache_base.is_floating_point() else d.cache_base.sum())
+        torch.cuda.synchronize()
+        want, _ = oracle.run_workload(wl, ws=torch.full_like(wl.workspace, -1.0))
+        assert torch.equal(ws.cpu().view(torch.uint8), want.view(torch.uint8)), rep

@@ -1,0 +1,88 @@
+"""CPU checks of the seeded workloads and of bench.py's host-side logic."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+import oracle
+import workloads
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_tiny_workload_shape_and_oracle():
+    wl = workloads.tiny_raw()
+    assert wl.num_reqs == 3 and wl.num_tokens == 88 and wl.block_size == 16
+    assert tuple(wl.block_table.shape) == (3, 8)
+    assert wl.cu_seq_lens.tolist() == [0, 17, 88, 88]
+    assert len(oracle.load().page_tasks(wl.cu_seq_lens, None, 3, 88, 16)) == 7
+    ws, rows = oracle.run_workload(wl)
+    assert rows == 88
+    assert wl.algorithmic_bytes() == 88 * 576 * 4 + 16
+
+
+def test_workloads_are_deterministic():
+    a, b = workloads.tiny_raw(), workloads.tiny_raw()
+    assert torch.equal(a.cache_base.view(torch.uint8), b.cache_base.view(torch.uint8))
+    assert torch.equal(a.block_table, b.block_table)
+
+
+def test_named_workload_sizes():
+    """The headline shapes: 960 and 4800 pages, the skew and mixed batches."""
+    o = oracle.load()
+    wl = workloads.single_60k_raw()
+    assert (wl.num_tokens, wl.num_blocks, wl.block_table.shape[1]) == (61440, 1200, 960)
+    assert wl.algorithmic_bytes() == 141557768
+    assert len(o.page_tasks(wl.cu_seq_lens, None, 1, 61440, 64)) == 960
+    wl = workloads.single_300k_upconvert()
+    assert (wl.num_tokens, wl.num_blocks, wl.cache_base.dtype) == (307200, 6000, torch.uint8)
+    assert wl.algorithmic_bytes() == 530841608
+    codes = wl.cache_base.flatten()[:1 << 20]
+    assert not bool(((codes == 0x7F) | (codes == 0xFF)).any())   # no NaN codes drawn
+    wl = workloads.skew8_raw_starts()
+    lens = workloads.SKEW8_LENS
+    starts = wl.seq_starts.tolist()
+    assert all(0 <= s <= n // 4 for s, n in zip(starts, lens))
+    assert wl.num_tokens == sum(n - s for n, s in zip(lens, starts))
+    assert wl.workspace.shape[0] == sum(lens)
+    wl = workloads.mixed_dequant_strided()
+    assert wl.num_reqs == 64 and wl.cache_base.shape[2] == 577 and wl.workspace.shape[1] == 580
+    assert wl.src_cache().stride() == (64 * 577, 577, 1) and wl.dst().stride() == (580, 1)
+    assert all(0 <= n <= 65536 for n in wl.context_lens)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    proc = subprocess.run([sys.executable, os.path.join(REPO, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr
+
+
+def test_bench_counter_summary(tmp_path, monkeypatch):
+    """Counter scaling: each counter is divided by its reading for the
+    calibration copies (the last 10 copy dispatches) of the same run."""
+    sys.path.insert(0, REPO)
+    import bench
+
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+    for kind, counter, gather_kib, copy_kib in (("fetch", "FETCH_SIZE", 34643.5, 131072.0),
+                                                ("write", "WRITE_SIZE", 69121.0, 262144.0)):
+        lines = [head]
+        d = 0
+        for _ in range(5):
+            d += 1
+            lines.append(f'{d},"pkvg::gather_pages_kernel<...>",{counter},{gather_kib}\n')
+        for _ in range(10):
+            d += 1
+            lines.append(f'{d},"__amd_rocclr_copyBuffer",{counter},{copy_kib}\n')
+        (tmp_path / f"{kind}_counter_collection.csv").write_text("".join(lines))
+    res = bench.summarize_counters(str(tmp_path), "tiny_raw", 256, "cmd")
+    assert res["fetch"]["scale"] == pytest.approx(2.0)
+    assert res["write"]["scale"] == pytest.approx(1.0)
+    assert res["hbm_bytes_per_launch"] == round(34643.5 * 1024 * 2 + 69121.0 * 1024)
+    saved = json.loads((tmp_path / "traffic_tiny_raw.json").read_text())
+    assert saved["kernel_source_sha"] == bench.kernel_source_hash()
