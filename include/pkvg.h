@@ -28,9 +28,12 @@
  *  - block_table is int32 [num_reqs, >= block_table_width] with row pitch
  *    block_table_ld; entry [r][l] is the physical block holding logical page
  *    l of request r.
- *  - cu_seq_lens is int32 [num_reqs + 1]: request r writes output rows
- *    [min(cu[r], T), min(cu[r+1], T)) with T = num_tokens (the clamps of the
- *    page-task map).  seq_starts is int32 [num_reqs] or NULL: request r reads
+ *  - cu_seq_lens is int32 [num_reqs + 1] with cu_terminal = 1: request r
+ *    writes output rows [min(cu[r], T), min(cu[r+1], T)) with T = num_tokens
+ *    (the clamps of the page-task map).  With cu_terminal = 0 it holds only
+ *    the num_reqs starts and the last request ends at T (the map's
+ *    has_terminal_start switch).  cu_terminal must be 0 or 1 (else
+ *    PKVG_E_SHAPE).  seq_starts is int32 [num_reqs] or NULL: request r reads
  *    its context from token seq_starts[r] on (0 when NULL); output row
  *    min(cu[r],T) + i takes token t = seq_starts[r] + i, i.e. slot
  *    t % block_size of physical block block_table[r][t / block_size].
@@ -98,7 +101,9 @@ extern "C" {
  *   dst               device, [num_tokens, >=entry]; dst_row_stride >= entry
  *   num_tokens        >= 0: T, rows of dst
  *   block_table       device int32; block_table_width >= 0; block_table_ld >= width
- *   cu_seq_lens       device int32 [num_reqs + 1]
+ *   cu_seq_lens       device int32 [num_reqs + cu_terminal]
+ *   cu_terminal       1: cu_seq_lens ends with a terminal entry; 0: the last
+ *                     request ends at num_tokens
  *   seq_starts        device int32 [num_reqs] or NULL
  *   num_reqs          >= 0
  *   stream            hipStream_t or NULL
@@ -113,7 +118,7 @@ int gather_cache(const void *src_cache, int32_t elem_bytes,
                  void *dst, int64_t num_tokens, int64_t dst_row_stride,
                  const int32_t *block_table, int32_t block_table_width,
                  int64_t block_table_ld,
-                 const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                 const int32_t *cu_seq_lens, int32_t cu_terminal, const int32_t *seq_starts,
                  int32_t num_reqs, void *stream);
 
 /*
@@ -140,7 +145,8 @@ int gather_maybe_dequant(const void *src_cache, int32_t kv_cache_dtype,
                          void *dst, int64_t num_tokens, int64_t dst_row_stride,
                          const int32_t *block_table, int32_t block_table_width,
                          int64_t block_table_ld,
-                         const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                         const int32_t *cu_seq_lens, int32_t cu_terminal,
+                         const int32_t *seq_starts,
                          int32_t num_reqs, const float *scale, void *stream);
 
 /*
@@ -156,7 +162,8 @@ int gather_upconvert_fp8(const void *src_cache,
                          void *dst, int64_t num_tokens, int64_t dst_row_stride,
                          const int32_t *block_table, int32_t block_table_width,
                          int64_t block_table_ld,
-                         const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                         const int32_t *cu_seq_lens, int32_t cu_terminal,
+                         const int32_t *seq_starts,
                          int32_t num_reqs, const float *scale, void *stream);
 
 /*
@@ -171,7 +178,7 @@ int gather_upconvert_fp8(const void *src_cache,
  * Tasks are ordered by request, then logical page.  A request that gathers no
  * rows contributes no task.
  *
- *   cu_seq_lens, seq_starts, num_reqs, num_tokens, block_size: as above
+ *   cu_seq_lens, cu_terminal, seq_starts, num_reqs, num_tokens, block_size: as above
  *   block_table, block_table_width, block_table_ld, num_blocks: as above
  *   tasks      device int32 [capacity * PKVG_TASK_INTS]
  *   capacity   >= 0 task records available
@@ -180,7 +187,7 @@ int gather_upconvert_fp8(const void *src_cache,
  * Errors: PKVG_E_NULL, PKVG_E_SHAPE, PKVG_E_STRIDE, PKVG_E_LIMIT, PKVG_E_HIP.
  * num_reqs == 0 still writes num_tasks[0] = 0.
  */
-int gather_page_tasks(const int32_t *cu_seq_lens, const int32_t *seq_starts,
+int gather_page_tasks(const int32_t *cu_seq_lens, int32_t cu_terminal, const int32_t *seq_starts,
                       int32_t num_reqs, int64_t num_tokens, int32_t block_size,
                       const int32_t *block_table, int32_t block_table_width,
                       int64_t block_table_ld, int64_t num_blocks,

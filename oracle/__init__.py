@@ -67,9 +67,9 @@ class Oracle:
         lib.oracle_dequant_e4m3fn_bf16.argtypes = [ctypes.c_uint8, f32]
         lib.oracle_dequant_e4m3fn_bf16.restype = ctypes.c_uint16
         lib.oracle_gather.argtypes = [i32, vp, i32, i64, i32, i32, i64, i64,
-                                      vp, i32, i64, i64, vp, i32, i64, vp, vp, i32, f32]
+                                      vp, i32, i64, i64, vp, i32, i64, vp, i32, vp, i32, f32]
         lib.oracle_gather.restype = i64
-        lib.oracle_page_tasks.argtypes = [vp, vp, i32, i64, i32, vp, i64]
+        lib.oracle_page_tasks.argtypes = [vp, i32, vp, i32, i64, i32, vp, i64]
         lib.oracle_page_tasks.restype = i64
         self.lib = lib
         self.path = path
@@ -92,39 +92,42 @@ class Oracle:
                block_size: int, entry: int, src_block_stride: int, src_token_stride: int,
                dst_bytes: np.ndarray, dst_elem_bytes: int, num_tokens: int, dst_row_stride: int,
                block_table, block_table_width: int, block_table_ld: int,
-               cu_seq_lens, seq_starts, num_reqs: int, scale: float = 1.0) -> int:
+               cu_seq_lens, seq_starts, num_reqs: int, scale: float = 1.0,
+               terminal: bool = True) -> int:
         """Per-token oracle gather into ``dst_bytes`` (in place); returns rows written.
 
         ``src_bytes`` / ``dst_bytes`` are flat uint8 arrays starting at element
         (0, 0, 0) / (0, 0); strides are in elements of their own array.
+        ``terminal``: cu_seq_lens holds num_reqs + 1 entries; otherwise
+        num_reqs entries and the last request ends at num_tokens.
         """
         assert src_bytes.dtype == np.uint8 and dst_bytes.dtype == np.uint8
         bt = _as_i32(block_table)
         cu = _as_i32(cu_seq_lens)
         ss = _as_i32(seq_starts)
-        assert cu.size >= num_reqs + 1
+        assert cu.size >= num_reqs + (1 if terminal else 0)
         assert ss is None or ss.size >= num_reqs
         return int(self.lib.oracle_gather(
             mode, _ptr(src_bytes), src_elem_bytes, num_blocks, block_size, entry,
             src_block_stride, src_token_stride, _ptr(dst_bytes), dst_elem_bytes,
             num_tokens, dst_row_stride, _ptr(bt), block_table_width, block_table_ld,
-            _ptr(cu), _ptr(ss), num_reqs, ctypes.c_float(scale)))
+            _ptr(cu), int(terminal), _ptr(ss), num_reqs, ctypes.c_float(scale)))
 
     def page_tasks(self, cu_seq_lens, seq_starts, num_reqs: int, num_tokens: int,
-                   block_size: int) -> np.ndarray:
+                   block_size: int, terminal: bool = True) -> np.ndarray:
         """Page tasks [num_tasks, 5] int32: (req_id, logical_block,
         page_token_begin, page_token_end, output_token_begin)."""
         cu = _as_i32(cu_seq_lens)
         ss = _as_i32(seq_starts)
-        count = self.lib.oracle_page_tasks(_ptr(cu), _ptr(ss), num_reqs, num_tokens,
-                                           block_size, None, 0)
+        count = self.lib.oracle_page_tasks(_ptr(cu), int(terminal), _ptr(ss), num_reqs,
+                                           num_tokens, block_size, None, 0)
         out = np.zeros((max(count, 1), 5), dtype=np.int32)
-        self.lib.oracle_page_tasks(_ptr(cu), _ptr(ss), num_reqs, num_tokens, block_size,
-                                   _ptr(out), count)
+        self.lib.oracle_page_tasks(_ptr(cu), int(terminal), _ptr(ss), num_reqs, num_tokens,
+                                   block_size, _ptr(out), count)
         return out[:count]
 
     def gather_tensors(self, mode: int, src_cache, dst, block_table, cu_seq_lens, seq_starts,
-                       num_reqs: int, scale: float = 1.0) -> int:
+                       num_reqs: int, scale: float = 1.0, terminal: bool = True) -> int:
         """Run the oracle on torch CPU tensors, writing ``dst`` in place.
 
         ``src_cache``: a (possibly strided) [num_blocks, block_size, entry] view;
@@ -151,7 +154,7 @@ class Oracle:
             dst.element_size(), dst.shape[0], dst.stride(0), bt.numpy(), bt.shape[1],
             bt.shape[1], cu_seq_lens.to(torch.int32).numpy(),
             None if seq_starts is None else seq_starts.to(torch.int32).numpy(),
-            num_reqs, scale)
+            num_reqs, scale, terminal)
 
 
 _default: Oracle | None = None
@@ -177,5 +180,5 @@ def run_workload(wl, ws=None):
     dst_view = ws[: wl.num_tokens, : wl.entry]
     mode = MODE_E4M3FN_TO_BF16 if wl.kind in workloads.FP8_KINDS else MODE_COPY
     rows = o.gather_tensors(mode, wl.src_cache(), dst_view, wl.block_table, wl.cu_seq_lens,
-                            wl.seq_starts, wl.num_reqs, wl.scale)
+                            wl.seq_starts, wl.num_reqs, wl.scale, wl.cu_terminal)
     return ws, rows

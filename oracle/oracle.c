@@ -96,6 +96,20 @@ static int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 static int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 /*
+ * End of request r's output extent before clamping: cu_seq_lens[r + 1] when
+ * the array holds num_reqs + 1 entries (terminal); otherwise the last request
+ * ends at num_tokens (the page-task map's has_terminal_start switch, section
+ * "key source snippets").
+ */
+static int64_t request_end(const int32_t *cu_seq_lens, int32_t r, int32_t num_reqs,
+                           int64_t num_tokens, int32_t terminal)
+{
+    if (terminal || r + 1 < num_reqs)
+        return cu_seq_lens[r + 1];
+    return num_tokens;
+}
+
+/*
  * The per-token gather: the definition the page's own tests compare every
  * kernel against (section "key source snippets", the reference built token
  * by token in test_cp_gather_cache_mla_large_uneven_sequences).  For request
@@ -124,13 +138,13 @@ int64_t oracle_gather(int32_t mode,
                       int64_t num_tokens, int64_t dst_row_stride,
                       const int32_t *block_table, int32_t block_table_width,
                       int64_t block_table_ld,
-                      const int32_t *cu_seq_lens, const int32_t *seq_starts,
+                      const int32_t *cu_seq_lens, int32_t terminal, const int32_t *seq_starts,
                       int32_t num_reqs, float scale)
 {
     int64_t rows_written = 0;
     for (int32_t r = 0; r < num_reqs; ++r) {
         int64_t b = min64(cu_seq_lens[r], num_tokens);
-        int64_t e = min64(cu_seq_lens[r + 1], num_tokens);
+        int64_t e = min64(request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal), num_tokens);
         int64_t n = max64(e - b, 0);
         int64_t s = seq_starts ? seq_starts[r] : 0;
         for (int64_t i = 0; i < n; ++i) {
@@ -181,14 +195,14 @@ int64_t oracle_gather(int32_t mode,
  * for cap tasks); the return value is the total number of tasks, which may
  * exceed cap (then only the first cap are written).
  */
-int64_t oracle_page_tasks(const int32_t *cu_seq_lens, const int32_t *seq_starts,
+int64_t oracle_page_tasks(const int32_t *cu_seq_lens, int32_t terminal, const int32_t *seq_starts,
                           int32_t num_reqs, int64_t num_tokens, int32_t block_size,
                           int32_t *out, int64_t cap)
 {
     int64_t count = 0;
     for (int32_t r = 0; r < num_reqs; ++r) {
         int64_t b = min64(cu_seq_lens[r], num_tokens);
-        int64_t e = min64(cu_seq_lens[r + 1], num_tokens);
+        int64_t e = min64(request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal), num_tokens);
         int64_t n = max64(e - b, 0);
         int64_t s = seq_starts ? seq_starts[r] : 0;
         int64_t first_page = s / block_size;

@@ -21,6 +21,8 @@ Entry points (names as in the C ABI):
 a view of wider rows is fine), ``dst`` a [num_tokens, entry] view (innermost
 stride 1), ``block_table`` int32 [batch, width] (row stride >= width),
 ``cu_seq_lens`` int32 [batch + 1], ``seq_starts`` int32 [batch] or None.
+A ``cu_seq_lens`` of exactly ``batch`` entries (or ``cu_terminal=False``)
+means the open-ended convention: the last request ends at ``num_tokens``.
 """
 from __future__ import annotations
 
@@ -46,12 +48,13 @@ PKVG_TASK_INTS = 8
 
 # the C entry points and their argument types, as declared in include/pkvg.h
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
-_CACHE_ARGS = [_i64, _i32, _i32, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _vp, _i32]
+_CACHE_ARGS = [_i64, _i32, _i32, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _i32, _vp, _i32]
 SIGNATURES = {
     "gather_cache": [_vp, _i32] + _CACHE_ARGS + [_vp],
     "gather_maybe_dequant": [_vp, _i32] + _CACHE_ARGS + [_vp, _vp],
     "gather_upconvert_fp8": [_vp] + _CACHE_ARGS + [_vp, _vp],
-    "gather_page_tasks": [_vp, _vp, _i32, _i64, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp],
+    "gather_page_tasks": [_vp, _i32, _vp, _i32, _i64, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp,
+                          _vp],
     "pkvg_status_string": [ctypes.c_int],
     "pkvg_last_hip_error": [],
 }
@@ -123,7 +126,19 @@ def _device_i32(t: torch.Tensor | None, name: str, dim: int) -> torch.Tensor | N
     return t
 
 
-def _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts):
+def _terminal(cu_seq_lens: torch.Tensor, batch_size: int, cu_terminal) -> int:
+    """1 when cu_seq_lens carries a terminal entry, 0 when the last request runs
+    to num_tokens; by default decided by its length."""
+    if cu_terminal is None:
+        cu_terminal = cu_seq_lens.numel() != batch_size
+    need = batch_size + (1 if cu_terminal else 0)
+    if cu_seq_lens.numel() < need:
+        raise ValueError(f"cu_seq_lens needs {need} entries")
+    return 1 if cu_terminal else 0
+
+
+def _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts,
+                cu_terminal=None):
     for name, t, d in (("src_cache", src_cache, 3), ("dst", dst, 2)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
@@ -137,15 +152,14 @@ def _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts
     num_blocks, block_size, entry = src_cache.shape
     if dst.shape[1] != entry:
         raise ValueError(f"dst has {dst.shape[1]} columns, cache rows gather {entry}")
-    if cu_seq_lens.numel() < batch_size + 1:
-        raise ValueError("cu_seq_lens needs batch_size + 1 entries")
+    terminal = _terminal(cu_seq_lens, batch_size, cu_terminal)
     if block_table.shape[0] < batch_size:
         raise ValueError("block_table needs batch_size rows")
     if seq_starts is not None and seq_starts.numel() < batch_size:
         raise ValueError("seq_starts needs batch_size entries")
     return [num_blocks, block_size, entry, src_cache.stride(0), src_cache.stride(1),
             _ptr(dst), dst.shape[0], dst.stride(0), _ptr(block_table), block_table.shape[1],
-            block_table.stride(0), _ptr(cu_seq_lens), _ptr(seq_starts), batch_size]
+            block_table.stride(0), _ptr(cu_seq_lens), terminal, _ptr(seq_starts), batch_size]
 
 
 class PreparedCall:
@@ -165,10 +179,12 @@ class PreparedCall:
             raise PkvgError(status, self._name)
 
 
-def _prepare_cache(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts, stream):
+def _prepare_cache(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts, stream,
+                   cu_terminal=None):
     if src_cache.element_size() != dst.element_size():
         raise TypeError("gather_cache copies bits: cache and dst element sizes must match")
-    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts)
+    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts,
+                       cu_terminal)
     return PreparedCall("gather_cache", [_ptr(src_cache), src_cache.element_size(), *args,
                                          _stream_handle() if stream is None else stream])
 
@@ -187,7 +203,7 @@ def _scale_tensor(scale) -> torch.Tensor:
 
 
 def _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size, kv_cache_dtype,
-                           scale, seq_starts, stream):
+                           scale, seq_starts, stream, cu_terminal=None):
     if dst.dtype != torch.bfloat16:
         raise TypeError("gather_maybe_dequant writes a bf16 destination")
     if kv_cache_dtype == "auto":
@@ -199,45 +215,50 @@ def _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size,
         code, sc = PKVG_KV_FP8_E4M3, _scale_tensor(scale)
     else:
         raise ValueError(f"unknown kv_cache_dtype {kv_cache_dtype!r}")
-    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts)
+    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts,
+                       cu_terminal)
     return PreparedCall("gather_maybe_dequant", [_ptr(src_cache), code, *args, _ptr(sc),
                                                  _stream_handle() if stream is None else stream])
 
 
 def _prepare_upconvert(src_cache, dst, block_table, cu_seq_lens, batch_size, scale, seq_starts,
-                       stream):
+                       stream, cu_terminal=None):
     if dst.dtype != torch.bfloat16:
         raise TypeError("gather_upconvert_fp8 writes a bf16 destination")
     _fp8_source(src_cache)
     sc = _scale_tensor(scale)
-    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts)
+    args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts,
+                       cu_terminal)
     return PreparedCall("gather_upconvert_fp8", [_ptr(src_cache), *args, _ptr(sc),
                                                  _stream_handle() if stream is None else stream])
 
 
 def gather_cache(src_cache: torch.Tensor, dst: torch.Tensor, block_table: torch.Tensor,
                  cu_seq_lens: torch.Tensor, batch_size: int,
-                 seq_starts: torch.Tensor | None = None) -> None:
+                 seq_starts: torch.Tensor | None = None, *, cu_terminal: bool | None = None) -> None:
     """Raw gather: dst rows = cache rows, bit for bit (same element size)."""
-    _prepare_cache(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts, None)()
+    _prepare_cache(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts, None,
+                   cu_terminal)()
 
 
 def gather_maybe_dequant(src_cache: torch.Tensor, dst: torch.Tensor, block_table: torch.Tensor,
                          cu_seq_lens: torch.Tensor, batch_size: int, kv_cache_dtype: str,
                          scale: torch.Tensor | None = None,
-                         seq_starts: torch.Tensor | None = None) -> None:
+                         seq_starts: torch.Tensor | None = None, *,
+                         cu_terminal: bool | None = None) -> None:
     """Gather into a bf16 dst; kv_cache_dtype 'auto' copies a bf16 cache,
     'fp8' dequantises e4m3fn codes with the per-tensor fp32 ``scale``."""
     _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size, kv_cache_dtype,
-                           scale, seq_starts, None)()
+                           scale, seq_starts, None, cu_terminal)()
 
 
 def gather_upconvert_fp8(src_cache: torch.Tensor, dst: torch.Tensor, block_table: torch.Tensor,
                          cu_seq_lens: torch.Tensor, batch_size: int, scale: torch.Tensor,
-                         seq_starts: torch.Tensor | None = None) -> None:
+                         seq_starts: torch.Tensor | None = None, *,
+                         cu_terminal: bool | None = None) -> None:
     """fp8 (e4m3fn) cache -> bf16 dst: bf16_rne(fp32(code) * scale)."""
     _prepare_upconvert(src_cache, dst, block_table, cu_seq_lens, batch_size, scale, seq_starts,
-                       None)()
+                       None, cu_terminal)()
 
 
 def prepare(entry_point: str, *args, **kwargs) -> PreparedCall:
@@ -259,7 +280,7 @@ def prepare(entry_point: str, *args, **kwargs) -> PreparedCall:
 def gather_page_tasks(cu_seq_lens: torch.Tensor, seq_starts: torch.Tensor | None,
                       batch_size: int, num_tokens: int, block_size: int,
                       block_table: torch.Tensor, num_blocks: int,
-                      capacity: int | None = None):
+                      capacity: int | None = None, *, cu_terminal: bool | None = None):
     """Run the page-task builder alone.  Returns (tasks int32 [capacity, 8],
     count int32 [1]), both on the device; rows past count are unspecified."""
     _device_i32(block_table, "block_table", 2)
@@ -270,8 +291,9 @@ def gather_page_tasks(cu_seq_lens: torch.Tensor, seq_starts: torch.Tensor | None
     dev = cu_seq_lens.device
     tasks = torch.empty((max(capacity, 1), PKVG_TASK_INTS), dtype=torch.int32, device=dev)
     count = torch.empty(1, dtype=torch.int32, device=dev)
+    terminal = _terminal(cu_seq_lens, batch_size, cu_terminal)
     _check(library().gather_page_tasks(
-        _ptr(cu_seq_lens), _ptr(seq_starts), batch_size, num_tokens, block_size,
+        _ptr(cu_seq_lens), terminal, _ptr(seq_starts), batch_size, num_tokens, block_size,
         _ptr(block_table), block_table.shape[1], block_table.stride(0), num_blocks,
         _ptr(tasks), capacity, _ptr(count), _stream_handle()), "gather_page_tasks")
     return tasks[:capacity], count

@@ -95,6 +95,7 @@ struct GatherParams {
   int64_t num_blocks;
   int64_t num_tokens;
   int32_t num_reqs;
+  int32_t cu_terminal;           // 1: cu_seq_lens has num_reqs + 1 entries; 0: the last request ends at num_tokens
   int32_t block_size;
   int32_t block_table_width;
   int32_t chunks_per_row;        // row chunks (kRows), or chunks per row of the flat span (kFlat)
@@ -157,8 +158,13 @@ __device__ __forceinline__ int32_t page_count(int64_t b, int64_t e, int64_t s, i
   return static_cast<int32_t>((s + n + bs - 1) / bs - s / bs);
 }
 
-__device__ __forceinline__ int64_t clamp_rows(int32_t cu, int64_t T) {
-  return cu < T ? static_cast<int64_t>(cu) : T;
+__device__ __forceinline__ int64_t clamp_rows(int64_t cu, int64_t T) { return cu < T ? cu : T; }
+
+// Unclamped output end of request r: the next cu_seq_lens entry, or num_tokens
+// for the last request when cu_seq_lens has no terminal entry.
+__device__ __forceinline__ int64_t request_end(const GatherParams& p, int32_t r) {
+  if (p.cu_terminal || r + 1 < p.num_reqs) return p.cu_seq_lens[r + 1];
+  return p.num_tokens;
 }
 
 // Exclusive scan over the workgroup; `tmp` holds NWAVES ints of LDS.
@@ -212,7 +218,7 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
   int32_t sum = 0;
   for (int32_t r = lo; r < hi; ++r) {
     const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
-    const int64_t e = clamp_rows(p.cu_seq_lens[r + 1], p.num_tokens);
+    const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
     const int32_t s = p.seq_starts ? p.seq_starts[r] : 0;
     const int32_t c = page_count(b, e, s, p.block_size);
     B[r] = static_cast<int32_t>(b);
@@ -229,7 +235,7 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
   }
   if (threadIdx.x == 0) {
     P[R] = total;
-    B[R] = static_cast<int32_t>(clamp_rows(p.cu_seq_lens[R], p.num_tokens));
+    B[R] = static_cast<int32_t>(clamp_rows(request_end(p, R - 1), p.num_tokens));
   }
   __syncthreads();
 }
@@ -251,10 +257,11 @@ __device__ __forceinline__ WavePrefix build_prefix_wave(const GatherParams& p) {
   const int lane = threadIdx.x & 63;
   const int32_t R = p.num_reqs;
   WavePrefix w;
-  int32_t cb = 0, ce = 0, st = 0;
+  int64_t cb = 0, ce = 0;
+  int32_t st = 0;
   if (lane < R) {
     cb = p.cu_seq_lens[lane];
-    ce = p.cu_seq_lens[lane + 1];
+    ce = request_end(p, lane);
     st = p.seq_starts ? p.seq_starts[lane] : 0;
   }
   w.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
@@ -609,7 +616,8 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(GatherParams 
     const int64_t lb0 = ts.s / p.block_size + blockIdx.x;
     ts.first_phys_raw = lb0 < p.block_table_width ? uniform(p.block_table[lb0]) : -1;
     ts.b = static_cast<int32_t>(clamp_rows(uniform(p.cu_seq_lens[0]), p.num_tokens));
-    ts.e = static_cast<int32_t>(clamp_rows(uniform(p.cu_seq_lens[1]), p.num_tokens));
+    ts.e = static_cast<int32_t>(
+        clamp_rows(p.cu_terminal ? uniform(p.cu_seq_lens[1]) : p.num_tokens, p.num_tokens));
     num_tasks = page_count(ts.b, ts.e, ts.s, p.block_size);
   } else if (ts.mode == kWaveRegs) {
     ts.wp = build_prefix_wave(p);
@@ -649,7 +657,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_page_counts_kernel(GatherPa
     int32_t c = 0;
     if (r < R) {
       const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
-      const int64_t e = clamp_rows(p.cu_seq_lens[r + 1], p.num_tokens);
+      const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
       const int32_t s = p.seq_starts ? p.seq_starts[r] : 0;
       c = page_count(b, e, s, p.block_size);
     }
@@ -673,7 +681,7 @@ __global__ __launch_bounds__(256) void expand_tasks_kernel(GatherParams p, const
   for (int32_t task = blockIdx.x * blockDim.x + threadIdx.x; task < n; task += gridDim.x * blockDim.x) {
     const int32_t r = find_request(P, R, task);
     const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
-    const int64_t e = clamp_rows(p.cu_seq_lens[r + 1], p.num_tokens);
+    const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
     const int64_t s = p.seq_starts ? p.seq_starts[r] : 0;
     const TaskGeom g = task_geometry(task - P[r], b, e, s, p.block_size);
     TaskRecord t;

@@ -52,9 +52,10 @@ int check_common(const void* src, int64_t num_blocks, int32_t block_size, int32_
                  int64_t src_block_stride, int64_t src_token_stride, void* dst,
                  int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
                  int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
-                 int32_t num_reqs, bool* nothing) {
+                 int32_t cu_terminal, int32_t num_reqs, bool* nothing) {
   *nothing = false;
   if (num_reqs < 0 || num_tokens < 0 || num_blocks < 0 || block_table_width < 0) return PKVG_E_SHAPE;
+  if (cu_terminal != 0 && cu_terminal != 1) return PKVG_E_SHAPE;
   if (block_size <= 0 || entry <= 0) return PKVG_E_SHAPE;
   if (src_block_stride < 0 || src_token_stride < 0 || dst_row_stride < entry ||
       block_table_ld < block_table_width)
@@ -170,12 +171,13 @@ int run_plan(Plan& pl, hipStream_t stream) {
 
 void fill_common(Plan& pl, const void* src, void* dst, const int32_t* block_table,
                  int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
-                 const int32_t* seq_starts, int32_t num_reqs, int64_t num_blocks, int32_t block_size,
-                 int64_t num_tokens) {
+                 int32_t cu_terminal, const int32_t* seq_starts, int32_t num_reqs, int64_t num_blocks,
+                 int32_t block_size, int64_t num_tokens) {
   pl.p.src = static_cast<const uint8_t*>(src);
   pl.p.dst = static_cast<uint8_t*>(dst);
   pl.p.block_table = block_table;
   pl.p.cu_seq_lens = cu_seq_lens;
+  pl.p.cu_terminal = cu_terminal;
   pl.p.seq_starts = seq_starts;
   pl.p.block_table_ld = block_table_ld;
   pl.p.block_table_width = block_table_width;
@@ -246,16 +248,16 @@ int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, 
                  int32_t entry, int64_t src_block_stride, int64_t src_token_stride, void* dst,
                  int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
                  int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
-                 const int32_t* seq_starts, int32_t num_reqs, void* stream) {
+                 int32_t cu_terminal, const int32_t* seq_starts, int32_t num_reqs, void* stream) {
   if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return PKVG_E_DTYPE;
   bool nothing;
   int st = check_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
                         num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                        cu_seq_lens, num_reqs, &nothing);
+                        cu_seq_lens, cu_terminal, num_reqs, &nothing);
   if (st != PKVG_OK || nothing) return st;
   Plan pl;
-  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, seq_starts,
-              num_reqs, num_blocks, block_size, num_tokens);
+  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, cu_terminal,
+              seq_starts, num_reqs, num_blocks, block_size, num_tokens);
   st = plan_copy(pl, src_cache, dst, elem_bytes, entry, src_block_stride, src_token_stride, dst_row_stride,
                  block_size);
   if (st != PKVG_OK) return st;
@@ -265,18 +267,18 @@ int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, 
 static int gather_fp8_common(const void* src_cache, int64_t num_blocks, int32_t block_size, int32_t entry,
                              int64_t src_block_stride, int64_t src_token_stride, void* dst,
                              int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
-                             int32_t block_table_width, int64_t block_table_ld,
-                             const int32_t* cu_seq_lens, const int32_t* seq_starts, int32_t num_reqs,
+                             int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
+                             int32_t cu_terminal, const int32_t* seq_starts, int32_t num_reqs,
                              const float* scale, void* stream) {
   bool nothing;
   int st = check_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
                         num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                        cu_seq_lens, num_reqs, &nothing);
+                        cu_seq_lens, cu_terminal, num_reqs, &nothing);
   if (st != PKVG_OK || nothing) return st;
   if (!scale) return PKVG_E_NULL;
   Plan pl;
-  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, seq_starts,
-              num_reqs, num_blocks, block_size, num_tokens);
+  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, cu_terminal,
+              seq_starts, num_reqs, num_blocks, block_size, num_tokens);
   pl.p.scale = scale;
   st = plan_fp8(pl, src_cache, dst, entry, src_block_stride, src_token_stride, dst_row_stride, block_size);
   if (st != PKVG_OK) return st;
@@ -287,34 +289,34 @@ int gather_maybe_dequant(const void* src_cache, int32_t kv_cache_dtype, int64_t 
                          int32_t block_size, int32_t entry, int64_t src_block_stride,
                          int64_t src_token_stride, void* dst, int64_t num_tokens, int64_t dst_row_stride,
                          const int32_t* block_table, int32_t block_table_width, int64_t block_table_ld,
-                         const int32_t* cu_seq_lens, const int32_t* seq_starts, int32_t num_reqs,
-                         const float* scale, void* stream) {
+                         const int32_t* cu_seq_lens, int32_t cu_terminal, const int32_t* seq_starts,
+                         int32_t num_reqs, const float* scale, void* stream) {
   if (kv_cache_dtype == PKVG_KV_AUTO)
     return gather_cache(src_cache, 2, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
                         num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                        cu_seq_lens, seq_starts, num_reqs, stream);
+                        cu_seq_lens, cu_terminal, seq_starts, num_reqs, stream);
   if (kv_cache_dtype != PKVG_KV_FP8_E4M3) return PKVG_E_DTYPE;
   return gather_fp8_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
                            num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                           cu_seq_lens, seq_starts, num_reqs, scale, stream);
+                           cu_seq_lens, cu_terminal, seq_starts, num_reqs, scale, stream);
 }
 
 int gather_upconvert_fp8(const void* src_cache, int64_t num_blocks, int32_t block_size, int32_t entry,
                          int64_t src_block_stride, int64_t src_token_stride, void* dst, int64_t num_tokens,
                          int64_t dst_row_stride, const int32_t* block_table, int32_t block_table_width,
-                         int64_t block_table_ld, const int32_t* cu_seq_lens, const int32_t* seq_starts,
-                         int32_t num_reqs, const float* scale, void* stream) {
+                         int64_t block_table_ld, const int32_t* cu_seq_lens, int32_t cu_terminal,
+                         const int32_t* seq_starts, int32_t num_reqs, const float* scale, void* stream) {
   return gather_fp8_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
                            num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                           cu_seq_lens, seq_starts, num_reqs, scale, stream);
+                           cu_seq_lens, cu_terminal, seq_starts, num_reqs, scale, stream);
 }
 
-int gather_page_tasks(const int32_t* cu_seq_lens, const int32_t* seq_starts, int32_t num_reqs,
-                      int64_t num_tokens, int32_t block_size, const int32_t* block_table,
+int gather_page_tasks(const int32_t* cu_seq_lens, int32_t cu_terminal, const int32_t* seq_starts,
+                      int32_t num_reqs, int64_t num_tokens, int32_t block_size, const int32_t* block_table,
                       int32_t block_table_width, int64_t block_table_ld, int64_t num_blocks, int32_t* tasks,
                       int64_t capacity, int32_t* num_tasks, void* stream) {
   if (num_reqs < 0 || num_tokens < 0 || block_size <= 0 || block_table_width < 0 || num_blocks < 0 ||
-      capacity < 0)
+      capacity < 0 || (cu_terminal != 0 && cu_terminal != 1))
     return PKVG_E_SHAPE;
   if (block_table_ld < block_table_width) return PKVG_E_STRIDE;
   if (!num_tasks || (num_reqs > 0 && (!cu_seq_lens || !block_table)) || (capacity > 0 && !tasks))
@@ -325,6 +327,7 @@ int gather_page_tasks(const int32_t* cu_seq_lens, const int32_t* seq_starts, int
   GatherParams p{};
   p.block_table = block_table;
   p.cu_seq_lens = cu_seq_lens;
+  p.cu_terminal = cu_terminal;
   p.seq_starts = seq_starts;
   p.block_table_ld = block_table_ld;
   p.block_table_width = block_table_width;

@@ -193,6 +193,22 @@ def check_gather_hand_worked(o):
         assert rows == case["rows_written"], (case["name"], rows)
 
 
+def check_gather_open_end_hand_worked(o):
+    g = _golden("hand_worked_gather.json")["open_end_cases"]
+    nb, bs = 4, 2
+    cache = np.array([[10 * pb + s for s in range(bs)] for pb in range(nb)], dtype=np.int16)
+    for case in g["cases"]:
+        bt = np.array(case["block_table"], dtype=np.int32)
+        dst = np.full(case["rows"], g["sentinel"], dtype=np.int16)
+        R = bt.shape[0]
+        rows = o.gather(oracle_mod.MODE_COPY, cache.view(np.uint8).reshape(-1), 2, nb, bs, 1,
+                        bs, 1, dst.view(np.uint8), 2, case["num_tokens"], 1, bt.reshape(-1),
+                        case["width"], bt.shape[1], case["cu_seq_lens"], case["seq_starts"], R,
+                        terminal=False)
+        assert dst.tolist() == case["expected"], (case["name"], dst.tolist())
+        assert rows == case["rows_written"], (case["name"], rows)
+
+
 def check_gather_fp8_hand_worked(o):
     g = _golden("hand_worked_gather.json")["fp8_case"]
     cache = np.array([[[int(x, 16) for x in row] for row in blk] for blk in g["cache_codes"]],
@@ -250,6 +266,10 @@ def random_small_workloads(seed: int, count: int):
             wl.workspace = wl.workspace[: max(T, 1)].clone()
         else:
             wl.workspace = torch.cat([wl.workspace, wl.fresh_workspace()[:2]])  # guard rows
+        # open-ended cu_seq_lens: drop the terminal entry; the last request then
+        # runs to num_tokens, which here is at most its terminal end
+        if ri(0, 4) == 0:
+            wl = wl.open_ended()
         # guard case: corrupt some table entries (out of range ids, -1)
         if ri(0, 3) == 0 and wl.block_table.numel() > 0:
             flat = wl.block_table.view(-1)
@@ -270,9 +290,11 @@ def torch_indexing_reference(wl) -> torch.Tensor:
     cu = wl.cu_seq_lens.tolist()
     T = wl.num_tokens
     bs = wl.block_size
-    for r in range(wl.num_reqs):
+    R = wl.num_reqs
+    for r in range(R):
+        end = cu[r + 1] if (wl.cu_terminal or r + 1 < R) else T
         b = min(cu[r], T)
-        n = max(min(cu[r + 1], T) - b, 0)
+        n = max(min(end, T) - b, 0)
         s = 0 if wl.seq_starts is None else int(wl.seq_starts[r])
         tok = torch.arange(s, s + n)
         lb = tok // bs
@@ -304,9 +326,11 @@ def pages_method_reference(wl) -> tuple[torch.Tensor, list]:
 
     def task_of(task_id):
         rel = task_id
-        for r in range(wl.num_reqs):
+        R = wl.num_reqs
+        for r in range(R):
             out_b = min(cu[r], T)
-            length = max(min(cu[r + 1], T) - out_b, 0)
+            out_e = min(cu[r + 1] if (wl.cu_terminal or r + 1 < R) else T, T)
+            length = max(out_e - out_b, 0)
             src_b = 0 if starts is None else starts[r]
             first = src_b // bs
             npages = -(-(src_b + length) // bs) - first
@@ -343,7 +367,8 @@ def _oracle_workspace(o, wl):
     mode = (oracle_mod.MODE_E4M3FN_TO_BF16 if wl.kind in workloads.FP8_KINDS
             else oracle_mod.MODE_COPY)
     rows = o.gather_tensors(mode, wl.src_cache(), ws[: wl.num_tokens, : wl.entry],
-                            wl.block_table, wl.cu_seq_lens, wl.seq_starts, wl.num_reqs, wl.scale)
+                            wl.block_table, wl.cu_seq_lens, wl.seq_starts, wl.num_reqs, wl.scale,
+                            wl.cu_terminal)
     return ws, rows
 
 
@@ -364,7 +389,7 @@ def check_gather_vs_page_method(o, seed=12, count=60):
         want, tasks = pages_method_reference(wl)
         assert _same_bytes(got, want), wl.name
         otasks = o.page_tasks(wl.cu_seq_lens, wl.seq_starts, wl.num_reqs, wl.num_tokens,
-                              wl.block_size)
+                              wl.block_size, wl.cu_terminal)
         assert [tuple(x) for x in otasks.tolist()] == tasks, wl.name
 
 
@@ -468,7 +493,8 @@ def check_page_task_coverage(o, seed=14, count=200):
 ALL_CHECKS = [
     check_decode_spec_values, check_decode_matches_torch, check_bf16_hand,
     check_bf16_matches_torch, check_dequant_worked, check_dequant_matches_torch,
-    check_dequant_power_of_two_exact, check_gather_hand_worked, check_gather_fp8_hand_worked,
+    check_dequant_power_of_two_exact, check_gather_hand_worked, check_gather_open_end_hand_worked,
+    check_gather_fp8_hand_worked,
     check_gather_vs_torch_indexing, check_gather_vs_page_method,
     check_self_identifying_invariants, check_page_task_closed_forms, check_page_task_coverage,
 ]

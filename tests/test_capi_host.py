@@ -52,11 +52,11 @@ FAKE = 0x10000  # never dereferenced: every call below returns before any HIP ca
 
 def _gc(lib, **kw):
     a = dict(src=FAKE, elem=2, nb=4, bs=16, entry=8, sbs=128, sts=8, dst=FAKE, T=10, drs=8,
-             bt=FAKE, W=2, ld=2, cu=FAKE, ss=None, R=1)
+             bt=FAKE, W=2, ld=2, cu=FAKE, term=1, ss=None, R=1)
     a.update(kw)
     return lib.gather_cache(a["src"], a["elem"], a["nb"], a["bs"], a["entry"], a["sbs"], a["sts"],
-                            a["dst"], a["T"], a["drs"], a["bt"], a["W"], a["ld"], a["cu"], a["ss"],
-                            a["R"], None)
+                            a["dst"], a["T"], a["drs"], a["bt"], a["W"], a["ld"], a["cu"], a["term"],
+                            a["ss"], a["R"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -68,6 +68,8 @@ def _gc(lib, **kw):
     (dict(T=-1), pkvg.PKVG_E_SHAPE),
     (dict(nb=-1), pkvg.PKVG_E_SHAPE),
     (dict(W=-1), pkvg.PKVG_E_SHAPE),
+    (dict(term=2), pkvg.PKVG_E_SHAPE),
+    (dict(term=-1), pkvg.PKVG_E_SHAPE),
     (dict(drs=7), pkvg.PKVG_E_STRIDE),
     (dict(sts=-1), pkvg.PKVG_E_STRIDE),
     (dict(sbs=-1), pkvg.PKVG_E_STRIDE),
@@ -86,18 +88,20 @@ def test_gather_cache_argument_checks(lib, kw, code):
 
 
 def test_maybe_dequant_argument_checks(lib):
-    args = [4, 16, 8, 128, 8, FAKE, 10, 8, FAKE, 2, 2, FAKE, None, 1]
+    args = [4, 16, 8, 128, 8, FAKE, 10, 8, FAKE, 2, 2, FAKE, 1, None, 1]
     assert lib.gather_maybe_dequant(FAKE, 7, *args, FAKE, None) == pkvg.PKVG_E_DTYPE
     assert lib.gather_maybe_dequant(FAKE, pkvg.PKVG_KV_FP8_E4M3, *args, None, None) == pkvg.PKVG_E_NULL
     assert lib.gather_upconvert_fp8(FAKE, *args, None, None) == pkvg.PKVG_E_NULL
-    no_work = [4, 16, 8, 128, 8, None, 0, 8, None, 2, 2, None, None, 1]
+    no_work = [4, 16, 8, 128, 8, None, 0, 8, None, 2, 2, None, 1, None, 1]
     assert lib.gather_upconvert_fp8(None, *no_work, None, None) == pkvg.PKVG_OK
-    bad_stride = [4, 16, 8, 128, 8, FAKE, 10, 7, FAKE, 2, 2, FAKE, None, 1]
+    bad_stride = [4, 16, 8, 128, 8, FAKE, 10, 7, FAKE, 2, 2, FAKE, 1, None, 1]
     assert lib.gather_upconvert_fp8(FAKE, *bad_stride, FAKE, None) == pkvg.PKVG_E_STRIDE
 
 
 def test_page_tasks_argument_checks(lib):
-    f = lib.gather_page_tasks
+    def f(*a):
+        return lib.gather_page_tasks(a[0], 1, *a[1:])
+
     assert f(FAKE, None, 1, 10, 0, FAKE, 2, 2, 4, FAKE, 8, FAKE, None) == pkvg.PKVG_E_SHAPE
     assert f(FAKE, None, 1, 10, 16, FAKE, 2, 1, 4, FAKE, 8, FAKE, None) == pkvg.PKVG_E_STRIDE
     assert f(FAKE, None, 1, 10, 16, FAKE, 2, 2, 4, FAKE, 8, None, None) == pkvg.PKVG_E_NULL
@@ -105,6 +109,8 @@ def test_page_tasks_argument_checks(lib):
     assert f(FAKE, None, 1, 10, 16, FAKE, 2, 2, 4, None, 8, FAKE, None) == pkvg.PKVG_E_NULL
     assert f(FAKE, None, 1, 10, 16, FAKE, 2, 2, 4, FAKE, 1 << 31, FAKE, None) == pkvg.PKVG_E_LIMIT
     assert f(FAKE, None, -1, 10, 16, FAKE, 2, 2, 4, FAKE, 8, FAKE, None) == pkvg.PKVG_E_SHAPE
+    assert lib.gather_page_tasks(FAKE, 3, None, 1, 10, 16, FAKE, 2, 2, 4, FAKE, 8, FAKE,
+                                 None) == pkvg.PKVG_E_SHAPE
 
 
 def test_binding_rejects_host_tensors():

@@ -336,3 +336,45 @@ def test_graph_replays(kind, R):
         torch.cuda.synchronize()
         want, _ = oracle.run_workload(wl, ws=torch.full_like(wl.workspace, -1.0))
         assert torch.equal(ws.cpu().view(torch.uint8), want.view(torch.uint8)), rep
+
+
+# ---------------------------------------------------------------------------
+# the open-ended cu_seq_lens convention (no terminal entry)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,kind", [(1, workloads.RAW), (7, workloads.UPCONVERT),
+                                    (200, workloads.DEQUANT_FP8), (1500, workloads.RAW)])
+def test_open_ended_cu_seq_lens(R, kind):
+    """cu_seq_lens holds only the R starts; the last request runs to num_tokens.
+    On the device the array is followed by a poisoned entry, so a kernel that
+    read a terminal entry would write the wrong rows.  Covers the single-request,
+    wave-register, LDS-prefix and task-table paths."""
+    import paged_kv_cache_device_amd as pkvg
+
+    g = torch.Generator("cpu").manual_seed(R + 7)
+    lens = torch.randint(1, 200, (R,), generator=g).tolist()
+    starts = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in lens]
+    wl = workloads.make_workload(f"open_{R}_{kind}", kind, lens, 16, 64,
+                                 sum(-(-n // 16) for n in lens) + 2, seed=R, starts=starts,
+                                 scale=0.05, workspace_rows=sum(lens) + 8).open_ended()
+    want, _ = oracle.run_workload(wl)
+    for poison in (0, 1 << 30):
+        log(f"[open-ended] R={R} kind={kind} poison={poison}")
+        d = wl.to(DEV)
+        padded = torch.full((R + 1,), poison, dtype=torch.int32, device=DEV)
+        padded[:R] = d.cu_seq_lens
+        d.cu_seq_lens = padded[:R]
+        ws = run_hip(d)
+        torch.cuda.synchronize()
+        assert torch.equal(ws.cpu().view(torch.uint8), want.view(torch.uint8))
+    # the builder alone, against the oracle's task list in the same convention
+    o = oracle.load()
+    tw = o.page_tasks(wl.cu_seq_lens, wl.seq_starts, R, wl.num_tokens, 16, terminal=False)
+    tw = tw[tw[:, 3] > tw[:, 2]]
+    d = wl.to(DEV)
+    tasks, count = pkvg.gather_page_tasks(d.cu_seq_lens, d.seq_starts, R, wl.num_tokens, 16,
+                                          d.block_table, wl.num_blocks)
+    torch.cuda.synchronize()
+    n = int(count.item())
+    assert n == len(tw)
+    assert np.array_equal(tasks[:n].cpu().numpy()[:, :5], tw)

@@ -24,8 +24,13 @@ MUTANTS = [
      "int64_t logical = (t + 1) / block_size;", 0),
     ("seq_starts ignored by the gather", "int64_t s = seq_starts ? seq_starts[r] : 0;",
      "int64_t s = 0;", 0),
-    ("end not clamped to num_tokens", "int64_t e = min64(cu_seq_lens[r + 1], num_tokens);",
-     "int64_t e = cu_seq_lens[r + 1];", 0),
+    ("end not clamped to num_tokens",
+     "int64_t e = min64(request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal), num_tokens);",
+     "int64_t e = request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal);", 0),
+    ("open-ended last request reads a terminal entry", "if (terminal || r + 1 < num_reqs)",
+     "if (1)", 0),
+    ("open-ended last request ends at its start", "    return num_tokens;\n}",
+     "    return cu_seq_lens[r];\n}", 0),
     ("table width guard dropped", "if (logical >= block_table_width)\n                continue;",
      "", 0),
     ("physical id upper guard off by one", "phys >= num_blocks", "phys > num_blocks", 0),
@@ -55,8 +60,9 @@ MUTANTS = [
      "task[3] = (int32_t)(copy_end - copy_begin);", 0),
     ("task map ignores seq_starts", "int64_t s = seq_starts ? seq_starts[r] : 0;",
      "int64_t s = 0;", 1),
-    ("task end not clamped to num_tokens", "int64_t e = min64(cu_seq_lens[r + 1], num_tokens);",
-     "int64_t e = cu_seq_lens[r + 1];", 1),
+    ("task end not clamped to num_tokens",
+     "int64_t e = min64(request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal), num_tokens);",
+     "int64_t e = request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal);", 1),
 ]
 
 

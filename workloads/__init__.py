@@ -60,6 +60,7 @@ class Workload:
     context_lens: list
     scale: float = 1.0
     scale_tensor: Optional[torch.Tensor] = None  # fp32 [1] for fp8 kinds
+    cu_terminal: bool = True  # False: cu_seq_lens holds R entries, the last request ends at T
 
     @property
     def num_reqs(self) -> int:
@@ -99,17 +100,34 @@ class Workload:
     def dst_elem_bytes(self) -> int:
         return self.workspace.element_size()
 
+    def request_ends(self) -> list:
+        """Each request's output end before clamping to num_tokens."""
+        cu = self.cu_seq_lens.cpu().tolist()
+        R = self.num_reqs
+        return [cu[r + 1] if (self.cu_terminal or r + 1 < R) else self.num_tokens
+                for r in range(R)]
+
     def gathered_rows(self) -> int:
         """Rows the request extents cover (before any guard skips)."""
         cu = self.cu_seq_lens.cpu().tolist()
         T = self.num_tokens
-        return sum(max(min(cu[r + 1], T) - min(cu[r], T), 0) for r in range(self.num_reqs))
+        ends = self.request_ends()
+        return sum(max(min(ends[r], T) - min(cu[r], T), 0) for r in range(self.num_reqs))
+
+    def open_ended(self) -> "Workload":
+        """The same workload with cu_seq_lens in the open-ended convention
+        (R entries; the last request runs to num_tokens)."""
+        d = dataclasses.replace(self)
+        d.cu_seq_lens = self.cu_seq_lens[: self.num_reqs].clone()
+        d.cu_terminal = False
+        return d
 
     def algorithmic_bytes(self) -> int:
         """Payload read + payload written + metadata read, for a full (unguarded) gather."""
         rows = self.gathered_rows()
         pay = rows * self.entry * (self.src_elem_bytes + self.dst_elem_bytes)
-        meta = 4 * (self.num_reqs + 1) + (4 * self.num_reqs if self.seq_starts is not None else 0)
+        meta = 4 * (self.num_reqs + int(self.cu_terminal)) + (
+            4 * self.num_reqs if self.seq_starts is not None else 0)
         return pay + meta
 
 
