@@ -70,9 +70,10 @@ extern "C" {
 #define PKVG_E_STRIDE 3 /* a stride is negative, or the destination rows overlap (dst_row_stride < entry),
                            or block_table_ld < block_table_width */
 #define PKVG_E_DTYPE 4  /* unsupported element size or kv_cache_dtype */
-#define PKVG_E_LIMIT 5  /* beyond an implementation limit: one page's rows span >= 2^31 bytes
-                           (block_size * row bytes, or (block_size - 1) * token stride + row bytes),
-                           or num_tokens / block_size + 2 * num_reqs >= 2^31 */
+#define PKVG_E_LIMIT 5  /* beyond an implementation limit: num_tokens >= 2^31; one page's rows
+                           span >= 2^31 bytes (block_size * row bytes, or (block_size - 1) *
+                           token stride + row bytes); or num_tokens / block_size + 2 * num_reqs
+                           >= 2^31 */
 #define PKVG_E_HIP 6    /* a HIP runtime call failed (launch or allocation); see pkvg_last_hip_error */
 
 /* kv_cache_dtype values for gather_maybe_dequant */

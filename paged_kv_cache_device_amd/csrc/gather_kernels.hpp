@@ -8,25 +8,29 @@
 // rows (partial first/last pages included) with wide vector accesses; the
 // fp8 variants convert to bf16 and write coalesced rows.  The page's task
 // fields (section "key source snippets": request, logical block, slot range
-// inside the page, first output row) are produced here by an exclusive scan
-// of per-request page counts and a binary search, instead of the page's
-// linear scan over requests.
+// inside the page, first output row) are produced here from an exclusive scan
+// of per-request page counts, instead of the page's linear scan over requests.
 //
 // Design for gfx950:
-//  * the scan lives in LDS once per workgroup; each wave then resolves its
-//    page itself (binary search over LDS) and holds the task and physical
-//    block in SGPRs (readfirstlane), so no second barrier is needed;
+//  * how a workgroup finds its page depends on the batch: one request needs
+//    no scan (its first block-table entry is fetched with the request extent);
+//    up to 64 requests are scanned in wave registers and found with a ballot;
+//    up to 1024 in LDS with a binary search; more use a task table built by
+//    two small kernels.  Task fields live in SGPRs (readfirstlane), so no
+//    barrier follows the lookup;
 //  * the hot loop moves 16-byte (dwordx4) chunks, consecutive lanes on
 //    consecutive chunks, so one wave instruction covers 1 KiB of a row span;
-//    a whole page's loads are in flight before the matching stores;
+//    a whole page's loads are in flight before the matching stores, with the
+//    nontemporal cache policy (each byte is touched once);
 //  * all addressing that can exceed 2^31 bytes (page bases, output row bases)
 //    is int64; in-page offsets are 32-bit (the host guarantees that a page's
 //    rows span < 2^31 bytes);
 //  * fp8 pages: each lane reads 8 codes (8 bytes) and writes 8 bf16 (16
 //    bytes): v_cvt_pk_f32_fp8 (OCP e4m3fn on gfx950), one v_mul_f32 by the
 //    scale, v_cvt_pk_bf16_f32 (round to nearest even);
-//  * every shape is a runtime argument; templates cover only the access
-//    width and whether a page's rows are one contiguous span.
+//  * every shape is a runtime argument; templates cover only the workgroup
+//    shape, the access width, and whether a page's rows are one contiguous
+//    span.
 #pragma once
 
 #include <hip/hip_runtime.h>

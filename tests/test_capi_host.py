@@ -79,6 +79,7 @@ def _gc(lib, **kw):
     (dict(bt=None), pkvg.PKVG_E_NULL),
     (dict(cu=None), pkvg.PKVG_E_NULL),
     (dict(T=(1 << 31) * 16), pkvg.PKVG_E_LIMIT),        # too many page tasks
+    (dict(T=1 << 31, bs=1 << 20, entry=1), pkvg.PKVG_E_LIMIT),  # rows past int32
     (dict(bs=1 << 20, entry=1 << 10, drs=1 << 10), pkvg.PKVG_E_LIMIT),  # a page spans >= 2^31 bytes
     (dict(R=0, src=None, dst=None, bt=None, cu=None), pkvg.PKVG_OK),   # no work: nothing enqueued
     (dict(T=0, src=None, dst=None, bt=None, cu=None), pkvg.PKVG_OK),
