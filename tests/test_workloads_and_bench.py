@@ -86,3 +86,26 @@ def test_bench_counter_summary(tmp_path, monkeypatch):
     assert res["hbm_bytes_per_launch"] == round(34643.5 * 1024 * 2 + 69121.0 * 1024)
     saved = json.loads((tmp_path / "traffic_tiny_raw.json").read_text())
     assert saved["kernel_source_sha"] == bench.kernel_source_hash()
+
+
+@pytest.mark.parametrize("name,parts", [("tiny_raw", 5), ("skew8_raw_seq_starts", 16)])
+def test_threaded_oracle_baseline_matches_oracle(name, parts):
+    """The CPU baseline's row-range split reproduces the oracle's output."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    sys.path.insert(0, REPO)
+    import bench
+
+    wl = workloads.named(name)
+    want, rows = oracle.run_workload(wl)
+    ws = wl.fresh_workspace()
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        got_rows = bench.oracle_threaded(wl, parts, ws)(pool)
+    assert got_rows == rows
+    assert torch.equal(ws.view(torch.uint8), want.view(torch.uint8))
+    open_wl = workloads.tiny_raw().open_ended()
+    want, _ = oracle.run_workload(open_wl)
+    ws = open_wl.fresh_workspace()
+    with ThreadPoolExecutor(max_workers=2) as pool:
+        bench.oracle_threaded(open_wl, 3, ws)(pool)
+    assert torch.equal(ws.view(torch.uint8), want.view(torch.uint8))
