@@ -19,10 +19,7 @@ thread_local int g_last_hip_error = 0;
 
 // Workgroups launched: one per task up to this cap; any grid is correct
 // because workgroups stride over tasks.
-#ifndef PKVG_MAX_GRID
-#define PKVG_MAX_GRID (1 << 20)
-#endif
-constexpr int64_t kMaxGrid = PKVG_MAX_GRID;
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -46,8 +43,8 @@ struct Plan {
   int64_t capacity = 0;   // upper bound on the number of page tasks
 };
 
-// Checks shared by every gather entry point.  Returns PKVG_OK and fills `plan`,
-// or an error code; `*nothing` is set when there is no work.
+// Checks shared by every gather entry point.  Returns PKVG_OK or an error
+// code; `*nothing` is set when there is no work (nothing is launched then).
 int check_common(const void* src, int64_t num_blocks, int32_t block_size, int32_t entry,
                  int64_t src_block_stride, int64_t src_token_stride, void* dst,
                  int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
@@ -81,16 +78,22 @@ int64_t max_bytes_stride(int64_t stride, int64_t elem) {
 // use the wide workgroup shape; fewer use the narrow one.
 constexpr int64_t kWideMinTasks = 1024;
 
+// hipLaunchKernel returns the launch's own status, so the calling thread's
+// error state (which other libraries use) is neither read nor cleared.
+template <typename... Args>
+hipError_t launch(void (*kernel)(Args...), unsigned grid, unsigned block, size_t lds, hipStream_t stream,
+                  Args... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), argv, lds, stream);
+}
+
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  if (grid >= kWideMinTasks) {
-    hipLaunchKernelGGL((pkvg::gather_pages_kernel<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>), dim3(grid),
-                       dim3(pkvg::Wide::threads), lds, stream, p);
-  } else {
-    hipLaunchKernelGGL((pkvg::gather_pages_kernel<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>), dim3(grid),
-                       dim3(pkvg::Narrow::threads), lds, stream, p);
-  }
-  return hipGetLastError();
+  if (grid >= kWideMinTasks)
+    return launch(pkvg::gather_pages_kernel<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>, grid, pkvg::Wide::threads,
+                  lds, stream, p);
+  return launch(pkvg::gather_pages_kernel<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>, grid,
+                pkvg::Narrow::threads, lds, stream, p);
 }
 
 template <int CONVERT, int W, bool SRC_VEC>
@@ -121,22 +124,19 @@ hipError_t dispatch(const Plan& pl, unsigned grid, size_t lds, hipStream_t strea
     case 8: return launch_layout<pkvg::kFp8Bf16, 8, false>(pl, grid, lds, stream);
     case 4: return launch_layout<pkvg::kFp8Bf16, 4, false>(pl, grid, lds, stream);
     case 2: return launch_layout<pkvg::kFp8Bf16, 2, false>(pl, grid, lds, stream);
-    default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, grid, lds, stream);
+    default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, grid, lds, stream);  // one code: any alignment
   }
 }
 
 // Builder for large batches and for gather_page_tasks: P scan, then records.
 hipError_t build_tasks(const GatherParams& p, int32_t* P, int32_t* count, TaskRecord* out,
                        int64_t capacity, hipStream_t stream) {
-  hipLaunchKernelGGL(pkvg::scan_page_counts_kernel, dim3(1), dim3(pkvg::kScanThreads), 0, stream, p, P,
-                     count);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch(pkvg::scan_page_counts_kernel, 1, pkvg::kScanThreads, 0, stream, p, P, count);
   if (e != hipSuccess || capacity == 0) return e;
   const int64_t blocks = (capacity + 255) / 256;
   const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
-  hipLaunchKernelGGL(pkvg::expand_tasks_kernel, dim3(grid), dim3(256), 0, stream, p, P, out,
-                     static_cast<int32_t>(capacity));
-  return hipGetLastError();
+  return launch(pkvg::expand_tasks_kernel, grid, 256, 0, stream, p, const_cast<const int32_t*>(P), out,
+                static_cast<int32_t>(capacity));
 }
 
 int run_plan(Plan& pl, hipStream_t stream) {
