@@ -131,9 +131,12 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t d, uint32_t m
 }
 
 // Native vector types: they stay in VGPRs through every transformation (the
-// HIP uint4/uint2 wrapper structs can end up in scratch memory).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// HIP uint4/uint2 wrapper structs can end up in scratch memory).  Declared with
+// 4-byte alignment: CDNA's multi-dword global accesses need only dword
+// alignment, so 16-byte chunks also serve rows whose pitch is a multiple of 4
+// (a 1160-byte bf16 row, say).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
 
 // Page data is touched exactly once: nontemporal loads and stores (the "nt"
 // cache policy) stream it through the caches without displacing other lines.
@@ -431,8 +434,6 @@ __device__ __forceinline__ PageSrc page_src(const uint8_t* ptr, uint32_t used_by
 // K (4 or 8) codes at byte `off` from base4, any alignment.  The window starts
 // at the dword holding byte `off`, or earlier when that would pass `lim`; the
 // codes then sit 0..4 bytes into it.  Needs lim >= 12 (K = 8) or 8 (K = 4).
-typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
-
 template <int K>
 __device__ __forceinline__ typename CodesOf<K>::T load_codes_window(const uint8_t* base4, uint32_t off,
                                                                    uint32_t lim) {
@@ -440,7 +441,7 @@ __device__ __forceinline__ typename CodesOf<K>::T load_codes_window(const uint8_
   const uint32_t a = min(off & ~3u, lim - kWin);
   const uint32_t sh = off - a;
   if constexpr (K == 8) {
-    const u32x2_a4 lo = load_stream<u32x2_a4>(base4 + a);
+    const u32x2 lo = load_stream<u32x2>(base4 + a);
     const uint32_t hi = load_stream<uint32_t>(base4 + a + 8);
     u32x2 w;
     w.x = sh == 4 ? lo.y : __builtin_amdgcn_alignbyte(lo.y, lo.x, sh);
@@ -448,7 +449,7 @@ __device__ __forceinline__ typename CodesOf<K>::T load_codes_window(const uint8_
     return w;
   } else {
     static_assert(K == 4, "windowed code loads take 4 or 8 codes");
-    const u32x2_a4 d = load_stream<u32x2_a4>(base4 + a);
+    const u32x2 d = load_stream<u32x2>(base4 + a);
     return sh == 4 ? d.y : __builtin_amdgcn_alignbyte(d.y, d.x, sh);
   }
 }

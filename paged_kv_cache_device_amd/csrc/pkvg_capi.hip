@@ -200,8 +200,13 @@ int plan_copy(Plan& pl, const void* src, void* dst, int64_t elem, int32_t entry,
   // in-page offsets are 32-bit: a page's source and destination rows span < 2^31 bytes
   if (int64_t(block_size) * row >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
   if (int64_t(block_size - 1) * st + row >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  // 16- and 8-byte chunks need rows of that many bytes and dword-aligned
+  // strides and bases; narrower chunks need their own alignment
+  auto fits = [&](int64_t a) {
+    return sb % a == 0 && st % a == 0 && dr % a == 0 && aligned(src, a) && aligned(dst, a);
+  };
   int w = 16;
-  while (w > 1 && (row % w || sb % w || st % w || dr % w || !aligned(src, w) || !aligned(dst, w))) w >>= 1;
+  while (w > 1 && (row % w || !fits(w < 4 ? w : 4))) w >>= 1;
   pl.convert = pkvg::kCopy;
   pl.width = w;
   pl.layout = (st == row && dr == row) ? pkvg::kFlat : pkvg::kRows;
@@ -221,10 +226,15 @@ int plan_fp8(Plan& pl, const void* src, void* dst, int32_t entry, int64_t sbs, i
   const int64_t dr = max_bytes_stride(drs_elems, 2);
   if (dr < 0) return PKVG_E_LIMIT;
   if (int64_t(block_size) * entry * 2 >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  // k codes per lane store 2k bytes of bf16: dword-aligned rows suffice for
+  // k >= 2 (multi-dword stores need only dword alignment), 2-byte rows for k = 1;
+  // their loads are k-byte words when the code rows are dword-aligned (k >= 4)
+  // or k-aligned (k < 4)
   int k = 8;
-  while (k > 1 && (entry % k || dr % (2 * k) || !aligned(dst, 2 * k))) k >>= 1;
+  while (k > 1 && (entry % k || dr % 4 || !aligned(dst, 4))) k >>= 1;
   pl.convert = pkvg::kFp8Bf16;
-  pl.src_vec = (sbs % k == 0) && (sts % k == 0) && aligned(src, k);
+  const int64_t src_align = k < 4 ? k : 4;
+  pl.src_vec = (sbs % src_align == 0) && (sts % src_align == 0) && aligned(src, src_align);
   // unaligned code rows are read as shifted dword windows, which need rows of
   // at least 16 codes; shorter unaligned rows use one code per lane
   if (!pl.src_vec && k >= 4 && entry < 16) k = 1;

@@ -73,14 +73,18 @@ RAW_PATHS = [
     (torch.bfloat16, 576, 576, 576),   # 16 B, flat
     (torch.bfloat16, 576, 640, 576),   # 16 B, rows (padded cache rows)
     (torch.bfloat16, 576, 576, 584),   # 16 B, rows (padded dst rows)
+    (torch.bfloat16, 576, 578, 580),   # 16 B, dword-aligned rows (1156 / 1160-byte pitch)
+    (torch.bfloat16, 576, 578, 578),   # 16 B, rows at every dword offset mod 16
     (torch.bfloat16, 12, 12, 12),      # 8 B (24-byte rows), flat
     (torch.bfloat16, 12, 16, 12),      # 8 B, rows
+    (torch.bfloat16, 12, 14, 14),      # 8 B, dword-aligned rows (28-byte pitch)
     (torch.bfloat16, 6, 6, 6),         # 4 B, flat
     (torch.bfloat16, 6, 8, 10),        # 4 B, rows
     (torch.bfloat16, 7, 7, 7),         # 2 B, flat
     (torch.bfloat16, 7, 9, 8),         # 2 B, rows
     (torch.uint8, 577, 577, 577),      # 1 B, flat
     (torch.uint8, 577, 579, 580),      # 1 B, rows
+    (torch.uint8, 576, 580, 588),      # 16 B, dword-aligned byte rows
     (torch.float32, 576, 576, 576),    # fp32 entries, 16 B flat
     (torch.float32, 3, 5, 3),          # fp32, 4 B rows
 ]
@@ -103,9 +107,11 @@ FP8_PATHS = [
     # (entry, cache cols, dst cols)
     (576, 576, 576),   # 8 codes, vector loads, flat
     (576, 584, 576),   # 8 codes, vector loads, rows
-    (576, 577, 576),   # 8 codes (dst 16-B aligned), byte loads, rows
-    (576, 577, 580),   # 4 codes, byte loads, rows (the strided mixed workload)
-    (576, 580, 580),   # 4 codes, vector loads, rows
+    (576, 577, 576),   # 8 codes, unaligned code rows (dword windows), rows
+    (576, 577, 580),   # 8 codes, windows, 1160-byte dst pitch (the strided mixed workload)
+    (576, 580, 580),   # 8 codes, dword-aligned code rows, 1160-byte dst pitch
+    (576, 578, 578),   # 8 codes, windows, dst rows at every dword offset mod 16
+    (20, 21, 22),      # 4 codes, windows, 44-byte dst pitch
     (12, 12, 12),      # 4 codes (24-byte dst rows), flat
     (6, 6, 6),         # 2 codes, flat
     (6, 7, 7),         # 1 code
