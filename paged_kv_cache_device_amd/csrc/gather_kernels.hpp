@@ -105,6 +105,7 @@ struct GatherParams {
   int32_t chunks_per_row;        // row chunks (kRows), or chunks per row of the flat span (kFlat)
   int32_t row_in_bytes;          // bytes of a source row that are gathered
   uint32_t chunks_magic;         // ceil(2^32 / chunks_per_row), or 0xFFFFFFFF for 1
+  uint32_t block_size_magic;     // ceil(2^32 / block_size), or 0xFFFFFFFF for 1
   int32_t task_capacity;         // with tasks: records available
 };
 
@@ -157,12 +158,20 @@ template <> struct VecOf<4> { using T = uint32_t; };
 template <> struct VecOf<2> { using T = uint16_t; };
 template <> struct VecOf<1> { using T = uint8_t; };
 
-// Page counts of one request: rows [b, e) of the output, source tokens from s.
-// A request with no rows has no pages.
-__device__ __forceinline__ int32_t page_count(int64_t b, int64_t e, int64_t s, int32_t bs) {
+// Token index -> logical page: floor(t / block_size) for 0 <= t < 2^32, a
+// multiply-high instead of a 64-bit division.  Token indices stay below 2^32:
+// a request starts below 2^31 and gathers fewer than 2^31 rows.
+__device__ __forceinline__ uint32_t page_of(const GatherParams& p, int64_t t) {
+  return div_magic(static_cast<uint32_t>(t), static_cast<uint32_t>(p.block_size), p.block_size_magic);
+}
+
+// Page counts of one request: rows [b, e) of the output, source tokens from s,
+// i.e. the pages holding tokens s .. s + (e - b) - 1.  A request with no rows
+// has no pages.
+__device__ __forceinline__ int32_t page_count(const GatherParams& p, int64_t b, int64_t e, int64_t s) {
   const int64_t n = e - b;
   if (n <= 0) return 0;
-  return static_cast<int32_t>((s + n + bs - 1) / bs - s / bs);
+  return static_cast<int32_t>(page_of(p, s + n - 1) - page_of(p, s) + 1);
 }
 
 __device__ __forceinline__ int64_t clamp_rows(int64_t cu, int64_t T) { return cu < T ? cu : T; }
@@ -227,7 +236,7 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
     const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
     const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
     const int32_t s = p.seq_starts ? p.seq_starts[r] : 0;
-    const int32_t c = page_count(b, e, s, p.block_size);
+    const int32_t c = page_count(p, b, e, s);
     B[r] = static_cast<int32_t>(b);
     S[r] = s;
     P[r] = c;
@@ -274,7 +283,7 @@ __device__ __forceinline__ WavePrefix build_prefix_wave(const GatherParams& p) {
   w.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
   w.e = static_cast<int32_t>(clamp_rows(ce, p.num_tokens));
   w.s = st;
-  w.count = lane < R ? page_count(w.b, w.e, w.s, p.block_size) : 0;
+  w.count = lane < R ? page_count(p, w.b, w.e, w.s) : 0;
   int32_t incl = w.count;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -306,9 +315,11 @@ struct TaskGeom {
   int64_t out_begin;
 };
 
-__device__ __forceinline__ TaskGeom task_geometry(int32_t j, int64_t b, int64_t e, int64_t s, int32_t bs) {
+__device__ __forceinline__ TaskGeom task_geometry(const GatherParams& p, int32_t j, int64_t b, int64_t e,
+                                                  int64_t s) {
+  const int32_t bs = p.block_size;
   const int64_t n = e - b > 0 ? e - b : 0;
-  const int64_t logical = s / bs + j;
+  const int64_t logical = static_cast<int64_t>(page_of(p, s)) + j;
   const int64_t page0 = logical * bs;
   const int64_t cb = s > page0 ? s : page0;
   const int64_t ce = (s + n) < (page0 + bs) ? (s + n) : (page0 + bs);
@@ -558,7 +569,7 @@ struct TaskSource {
 // Resolve `task` (the same for every lane) to its page, all fields wave-uniform.
 __device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSource& ts, int32_t task) {
   if (ts.mode == kSingle) {
-    const TaskGeom g = task_geometry(task, ts.b, ts.e, ts.s, p.block_size);
+    const TaskGeom g = task_geometry(p, task, ts.b, ts.e, ts.s);
     int64_t phys;
     if (task == static_cast<int32_t>(blockIdx.x)) {
       phys = g.logical < p.block_table_width ? ts.first_phys_raw : -1;
@@ -575,13 +586,13 @@ __device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSo
     const int32_t e = uniform(__builtin_amdgcn_readlane(ts.wp.e, r));
     const int32_t s = uniform(__builtin_amdgcn_readlane(ts.wp.s, r));
     const int32_t first = uniform(__builtin_amdgcn_readlane(ts.wp.incl - ts.wp.count, r));
-    const TaskGeom g = task_geometry(task - first, b, e, s, p.block_size);
+    const TaskGeom g = task_geometry(p, task - first, b, e, s);
     return page_from(p, uniform64(lookup_block(p, r, g.logical)), g.pbeg, g.pend, g.out_begin);
   }
   if (ts.mode == kLdsPrefix) {
     const int32_t r = uniform(find_request(ts.P, p.num_reqs, task));
-    const TaskGeom g = task_geometry(task - uniform(ts.P[r]), uniform(ts.B[r]), uniform(ts.B[r + 1]),
-                                     uniform(ts.S[r]), p.block_size);
+    const TaskGeom g = task_geometry(p, task - uniform(ts.P[r]), uniform(ts.B[r]), uniform(ts.B[r + 1]),
+                                     uniform(ts.S[r]));
     return page_from(p, uniform64(lookup_block(p, r, g.logical)), g.pbeg, g.pend, g.out_begin);
   }
   const TaskRecord t = p.tasks[task];
@@ -618,12 +629,12 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(GatherParams 
     // its block-table entry is requested together with the request extent
     // instead of after it (one dependent memory round trip less).
     ts.s = p.seq_starts ? uniform(p.seq_starts[0]) : 0;
-    const int64_t lb0 = ts.s / p.block_size + blockIdx.x;
+    const int64_t lb0 = static_cast<int64_t>(page_of(p, ts.s)) + blockIdx.x;
     ts.first_phys_raw = lb0 < p.block_table_width ? uniform(p.block_table[lb0]) : -1;
     ts.b = static_cast<int32_t>(clamp_rows(uniform(p.cu_seq_lens[0]), p.num_tokens));
     ts.e = static_cast<int32_t>(
         clamp_rows(p.cu_terminal ? uniform(p.cu_seq_lens[1]) : p.num_tokens, p.num_tokens));
-    num_tasks = page_count(ts.b, ts.e, ts.s, p.block_size);
+    num_tasks = page_count(p, ts.b, ts.e, ts.s);
   } else if (ts.mode == kWaveRegs) {
     ts.wp = build_prefix_wave(p);
     num_tasks = ts.wp.total;
@@ -664,7 +675,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_page_counts_kernel(GatherPa
       const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
       const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
       const int32_t s = p.seq_starts ? p.seq_starts[r] : 0;
-      c = page_count(b, e, s, p.block_size);
+      c = page_count(p, b, e, s);
     }
     int32_t total;
     const int32_t off = block_exclusive_scan<kScanThreads>(c, scan_tmp, total);
@@ -688,7 +699,7 @@ __global__ __launch_bounds__(256) void expand_tasks_kernel(GatherParams p, const
     const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
     const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
     const int64_t s = p.seq_starts ? p.seq_starts[r] : 0;
-    const TaskGeom g = task_geometry(task - P[r], b, e, s, p.block_size);
+    const TaskGeom g = task_geometry(p, task - P[r], b, e, s);
     TaskRecord t;
     t.req = r;
     t.logical = g.logical;

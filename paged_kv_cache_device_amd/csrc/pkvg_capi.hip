@@ -186,6 +186,7 @@ void fill_common(Plan& pl, const void* src, void* dst, const int32_t* block_tabl
   pl.p.num_reqs = num_reqs;
   pl.p.num_blocks = num_blocks;
   pl.p.block_size = block_size;
+  pl.p.block_size_magic = magic_for(static_cast<uint32_t>(block_size));
   pl.p.num_tokens = num_tokens;
   pl.capacity = num_tokens / block_size + 2 * int64_t(num_reqs) + 1;
 }
@@ -346,6 +347,7 @@ int gather_page_tasks(const int32_t* cu_seq_lens, int32_t cu_terminal, const int
   p.num_reqs = num_reqs;
   p.num_blocks = num_blocks;
   p.block_size = block_size;
+  p.block_size_magic = magic_for(static_cast<uint32_t>(block_size));
   p.num_tokens = num_tokens;
   void* scratch = nullptr;
   hipError_t e = hipMallocAsync(&scratch, sizeof(int32_t) * (size_t(num_reqs) + 1), s);
