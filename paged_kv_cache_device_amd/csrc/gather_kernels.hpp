@@ -131,6 +131,10 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t d, uint32_t m
   return q;
 }
 
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format;
+// no swizzle, no index stride).
+constexpr int32_t kBufferWord3 = 0x00020000;
+
 // Native vector types: they stay in VGPRs through every transformation (the
 // HIP uint4/uint2 wrapper structs can end up in scratch memory).  Declared with
 // 4-byte alignment: CDNA's multi-dword global accesses need only dword
@@ -600,40 +604,77 @@ __device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSo
                    static_cast<int64_t>(uniform(t.out_begin)));
 }
 
+// One int32 read through the vector memory path.  Its wait (vmcnt) leaves the
+// scalar loads in flight alone: scalar loads complete in any order, so waiting
+// for one scalar load waits for all of them, kernel arguments included.
+__device__ __forceinline__ int32_t load_i32_vector_path(const int32_t* q) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(q), 0, 4, kBufferWord3);
+  return uniform(__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
+
 // CONVERT == kCopy: W = bytes per lane access.  CONVERT == kFp8Bf16: W = codes
 // per lane access.  Grid: any size (the host launches one workgroup per task);
 // workgroup w takes tasks w, w + gridDim.x, ...  Dynamic LDS (LDS-prefix mode,
 // 64 < num_reqs): (3 * num_reqs + 2) int32.
+//
+// The leading scalar arguments repeat the fields of `params` that the task
+// lookup needs first, and `mode` is the TaskMode the host chose.  Leading
+// scalars are preloaded into SGPRs when a wave starts (gfx950 kernarg
+// preloading), so the metadata loads go out without waiting for a kernel
+// argument fetch; the struct arrives while they are in flight.
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
-__global__ __launch_bounds__(SH::threads) void gather_pages_kernel(GatherParams p) {
+__global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
+    const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts, int32_t mode,
+    int32_t num_reqs, int32_t block_size, uint32_t block_size_magic, int32_t block_table_width,
+    int32_t cu_terminal, int64_t num_tokens, GatherParams params) {
   using M = Mover<CONVERT, W, LAYOUT, SRC_VEC>;
+  GatherParams p = params;
+  p.cu_seq_lens = cu_seq_lens;
+  p.block_table = block_table;
+  p.seq_starts = seq_starts;
+  p.num_reqs = num_reqs;
+  p.block_size = block_size;
+  p.block_size_magic = block_size_magic;
+  p.block_table_width = block_table_width;
+  p.cu_terminal = cu_terminal;
+  p.num_tokens = num_tokens;
   extern __shared__ int32_t lds[];
   __shared__ int32_t scan_tmp[SH::waves];
 
   const int32_t R = p.num_reqs;
   TaskSource ts;
-  ts.mode = p.tasks != nullptr ? kTable : (R == 1 ? kSingle : (R <= kWaveMaxReqs ? kWaveRegs : kLdsPrefix));
+  ts.mode = mode;
   int32_t* P = lds;
   int32_t* B = lds + (R + 1);
   int32_t* S = lds + 2 * (R + 1);
   ts.P = P;
   ts.B = B;
   ts.S = S;
-  float scale = 1.0f;
-  if constexpr (CONVERT == kFp8Bf16)
-    scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*p.scale)));
 
   int32_t num_tasks;
   if (ts.mode == kSingle) {
     // The first page's logical block is seq_start / block_size + blockIdx.x:
     // its block-table entry is requested together with the request extent
-    // instead of after it (one dependent memory round trip less).
-    ts.s = p.seq_starts ? uniform(p.seq_starts[0]) : 0;
-    const int64_t lb0 = static_cast<int64_t>(page_of(p, ts.s)) + blockIdx.x;
-    ts.first_phys_raw = lb0 < p.block_table_width ? uniform(p.block_table[lb0]) : -1;
-    ts.b = static_cast<int32_t>(clamp_rows(uniform(p.cu_seq_lens[0]), p.num_tokens));
-    ts.e = static_cast<int32_t>(
-        clamp_rows(p.cu_terminal ? uniform(p.cu_seq_lens[1]) : p.num_tokens, p.num_tokens));
+    // instead of after it (one dependent memory round trip less).  Every load
+    // here is unconditional (an always-valid address stands in for an absent
+    // one) and the start goes through the vector path, so without seq_starts
+    // nothing waits before the entry and the extent are requested.
+    ts.s = p.seq_starts ? load_i32_vector_path(p.seq_starts) : 0;
+    const uint32_t lb0 = page_of(p, ts.s) + blockIdx.x;
+    const bool in_row = lb0 < static_cast<uint32_t>(p.block_table_width);
+    const int32_t* entry_at = in_row ? p.block_table + lb0 : p.cu_seq_lens;
+    const int32_t* end_at = p.cu_seq_lens + p.cu_terminal;  // cu_terminal is 0 or 1
+    const int32_t raw = uniform(*entry_at);
+    const int32_t cb = uniform(p.cu_seq_lens[0]);
+    const int32_t ce = uniform(*end_at);
+    // The page copy's kernel arguments are fetched while those loads are in
+    // flight: the empty asm needs them in SGPRs before the loaded values are
+    // used, so the compiler cannot leave their fetch for after that wait.
+    asm volatile("" ::"s"(p.src), "s"(p.dst), "s"(p.src_block_stride), "s"(p.src_token_stride),
+                 "s"(p.dst_row_stride), "s"(p.num_blocks), "s"(p.row_in_bytes), "s"(p.chunks_per_row));
+    ts.first_phys_raw = in_row ? raw : -1;
+    ts.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
+    ts.e = static_cast<int32_t>(clamp_rows(p.cu_terminal ? ce : p.num_tokens, p.num_tokens));
     num_tasks = page_count(p, ts.b, ts.e, ts.s);
   } else if (ts.mode == kWaveRegs) {
     ts.wp = build_prefix_wave(p);
@@ -645,6 +686,9 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(GatherParams 
     num_tasks = min(*p.task_count, p.task_capacity);
   }
   num_tasks = uniform(num_tasks);
+  float scale = 1.0f;
+  if constexpr (CONVERT == kFp8Bf16)
+    scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*p.scale)));
 
   const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
   for (int32_t task = blockIdx.x; task < num_tasks; task += gridDim.x) {

@@ -87,13 +87,25 @@ hipError_t launch(void (*kernel)(Args...), unsigned grid, unsigned block, size_t
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), argv, lds, stream);
 }
 
+// Where the gather kernel finds its page tasks: a prebuilt table, one request,
+// or a prefix built in wave registers (small batches) or LDS.
+int32_t task_mode(const GatherParams& p) {
+  if (p.tasks != nullptr) return pkvg::kTable;
+  if (p.num_reqs == 1) return pkvg::kSingle;
+  return p.num_reqs <= pkvg::kWaveMaxReqs ? pkvg::kWaveRegs : pkvg::kLdsPrefix;
+}
+
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+hipError_t launch_shape(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
+  return launch(pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC>, grid, SH::threads, lds, stream,
+                p.cu_seq_lens, p.block_table, p.seq_starts, task_mode(p), p.num_reqs, p.block_size,
+                p.block_size_magic, p.block_table_width, p.cu_terminal, p.num_tokens, p);
+}
+
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  if (grid >= kWideMinTasks)
-    return launch(pkvg::gather_pages_kernel<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>, grid, pkvg::Wide::threads,
-                  lds, stream, p);
-  return launch(pkvg::gather_pages_kernel<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>, grid,
-                pkvg::Narrow::threads, lds, stream, p);
+  if (grid >= kWideMinTasks) return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  return launch_shape<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
 }
 
 template <int CONVERT, int W, bool SRC_VEC>
