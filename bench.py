@@ -27,9 +27,10 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, REPO)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "effective HBM GB/s (read+write) and % of peak; median gather latency, 1 GPU"
 DEFAULT_WORKLOAD = "single_60k_raw"
 TRAFFIC_DIR = os.path.join(REPO, "profiles")
-KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp",
+KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp", "paged_kv_cache_device_amd/build.py",
                   "paged_kv_cache_device_amd/csrc/pkvg_capi.hip"]
 
 
@@ -177,8 +178,9 @@ def cold_latency(wl_dev, reps: int, scrub_bytes: int = 1 << 30):
 
 
 def copy_reference(nbytes_each_way: int, device, steps: int, min_bytes: int):
-    """A plain device-to-device copy of the same payload (torch copy kernel),
-    cold by rotation: the achievable-copy reference."""
+    """A plain device-to-device copy of the same payload (torch's copy_ of
+    contiguous same-dtype tensors, i.e. hipMemcpyAsync device to device), cold
+    by rotation: the achievable-copy reference."""
     import torch
 
     n = max(2, -(-min_bytes // (2 * nbytes_each_way)))
@@ -272,7 +274,20 @@ def cpu_baseline(wl, seconds: float = 10.0, threads: int = 1):
     return {"value": wl.algorithmic_bytes() / per / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"whole workload ({wl.name}), {reps} repetitions in {el:.1f} s, "
-                      f"{per * 1e3:.1f} ms each, {threads} thread(s) over disjoint row ranges"}
+                      f"{per * 1e3:.1f} ms each, {threads} thread(s) over disjoint row ranges, "
+                      f"on {cpu_model_name()}"}
+
+
+def cpu_model_name() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" if absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def host_threads() -> int:
@@ -362,7 +377,7 @@ def main():
 
     traffic = measured_traffic(args.workload)
     result = {
-        "metric": "effective HBM GB/s (read+write), cold cache",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -372,7 +387,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.kind == workloads.RAW else "fp8->bf16",
+        # raw gathers copy bytes; the fp8 paths decode and scale in fp32
+        "dtype": "u8" if wl.kind == workloads.RAW else "f32",
         "data": "synthetic (seeded N(0,1) bf16 / uniform non-NaN e4m3fn codes; shuffled blocks)",
         "config": {"workload": wl.name, "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
                    "block_size": wl.block_size, "entry": wl.entry,

@@ -48,6 +48,13 @@ def test_named_workload_sizes():
     assert all(0 <= s <= n // 4 for s, n in zip(starts, lens))
     assert wl.num_tokens == sum(n - s for n, s in zip(lens, starts))
     assert wl.workspace.shape[0] == sum(lens)
+    for k, wl in ((2, workloads.skew2_raw_starts()), (4, workloads.skew4_raw_starts())):
+        lens = workloads.SKEW8_LENS[:k]
+        starts = wl.seq_starts.tolist()
+        assert wl.num_reqs == k and wl.context_lens == lens
+        assert all(0 <= s <= n // 4 for s, n in zip(starts, lens))
+        assert wl.num_tokens == sum(n - s for n, s in zip(lens, starts))
+        assert wl.workspace.shape[0] == sum(lens)
     wl = workloads.mixed_dequant_strided()
     assert wl.num_reqs == 64 and wl.cache_base.shape[2] == 577 and wl.workspace.shape[1] == 580
     assert wl.src_cache().stride() == (64 * 577, 577, 1) and wl.dst().stride() == (580, 1)

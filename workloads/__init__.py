@@ -275,6 +275,24 @@ def skew8_raw_starts() -> Workload:
                          workspace_rows=sum(SKEW8_LENS))
 
 
+def skew_raw_starts(k: int, seed: int) -> Workload:
+    """The skew-k scenario: the first k lengths of the skew-8 list, with the same
+    seq_start rule, block size, entry, cache size and table width as skew-8."""
+    lens = SKEW8_LENS[:k]
+    return make_workload(f"skew{k}_raw_seq_starts", RAW, lens, 64, 576, 3000, seed=seed,
+                         width=2048, draw_starts_quarter=True, workspace_rows=sum(lens))
+
+
+def skew2_raw_starts() -> Workload:
+    """2 requests {131072, 16384} with seq_starts (skew-k reading, k = 2)."""
+    return skew_raw_starts(2, 1006)
+
+
+def skew4_raw_starts() -> Workload:
+    """4 requests {131072, 16384, 4096, 1024} with seq_starts (skew-k reading, k = 4)."""
+    return skew_raw_starts(4, 1007)
+
+
 def mixed_dequant_strided() -> Workload:
     """64 requests with log-normal lengths (median 4096, sigma 0.5, clipped to [0, 65536]),
     block 64, fp8 cache rows of 577 bytes using the first 576, scale 0.05, dequantised into
@@ -293,6 +311,8 @@ NAMED = {
     "single_60k_raw": single_60k_raw,
     "single_300k_fp8_upconvert": single_300k_upconvert,
     "skew8_raw_seq_starts": skew8_raw_starts,
+    "skew2_raw_seq_starts": skew2_raw_starts,
+    "skew4_raw_seq_starts": skew4_raw_starts,
     "mixed_fp8_dequant_strided": mixed_dequant_strided,
 }
 
