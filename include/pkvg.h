@@ -27,7 +27,8 @@
  *    may be written.
  *  - block_table is int32 [num_reqs, >= block_table_width] with row pitch
  *    block_table_ld; entry [r][l] is the physical block holding logical page
- *    l of request r.
+ *    l of request r.  With block_table_width == 0 it is never read and may be
+ *    NULL (every page then fails the width guard).
  *  - cu_seq_lens is int32 [num_reqs + 1] with cu_terminal = 1: request r
  *    writes output rows [min(cu[r], T), min(cu[r+1], T)) with T = num_tokens
  *    (the clamps of the page-task map).  With cu_terminal = 0 it holds only
@@ -109,9 +110,9 @@ extern "C" {
  *   num_reqs          >= 0
  *   stream            hipStream_t or NULL
  *
- * Errors: PKVG_E_NULL (src_cache, dst, block_table or cu_seq_lens NULL with
- * work to do), PKVG_E_SHAPE, PKVG_E_STRIDE, PKVG_E_DTYPE (elem_bytes),
- * PKVG_E_LIMIT, PKVG_E_HIP.
+ * Errors: PKVG_E_NULL (src_cache, dst or cu_seq_lens NULL, or block_table
+ * NULL with block_table_width > 0, while there is work to do), PKVG_E_SHAPE,
+ * PKVG_E_STRIDE, PKVG_E_DTYPE (elem_bytes), PKVG_E_LIMIT, PKVG_E_HIP.
  */
 int gather_cache(const void *src_cache, int32_t elem_bytes,
                  int64_t num_blocks, int32_t block_size, int32_t entry,

@@ -61,7 +61,8 @@ int check_common(const void* src, int64_t num_blocks, int32_t block_size, int32_
     *nothing = true;
     return PKVG_OK;
   }
-  if (!src || !dst || !block_table || !cu_seq_lens) return PKVG_E_NULL;
+  // a table with no columns is never read (every page fails the width guard)
+  if (!src || !dst || !cu_seq_lens || (!block_table && block_table_width > 0)) return PKVG_E_NULL;
   // output rows are int32, like the cu_seq_lens entries that address them
   if (num_tokens > INT32_MAX) return PKVG_E_LIMIT;
   // page tasks: at most floor(T / bs) + 2 per request (non-decreasing cu_seq_lens)
@@ -344,7 +345,8 @@ int gather_page_tasks(const int32_t* cu_seq_lens, int32_t cu_terminal, const int
       capacity < 0 || (cu_terminal != 0 && cu_terminal != 1))
     return PKVG_E_SHAPE;
   if (block_table_ld < block_table_width) return PKVG_E_STRIDE;
-  if (!num_tasks || (num_reqs > 0 && (!cu_seq_lens || !block_table)) || (capacity > 0 && !tasks))
+  if (!num_tasks || (num_reqs > 0 && (!cu_seq_lens || (!block_table && block_table_width > 0))) ||
+      (capacity > 0 && !tasks))
     return PKVG_E_NULL;
   if (capacity >= (int64_t(1) << 31) || num_tokens > INT32_MAX) return PKVG_E_LIMIT;
   if (num_tokens / block_size + 2 * int64_t(num_reqs) + 1 >= (int64_t(1) << 31)) return PKVG_E_LIMIT;

@@ -291,6 +291,40 @@ def test_single_request(tokens, start, bs, kind):
     check_parity(wl, DEV)
 
 
+@pytest.mark.parametrize("kind", [workloads.RAW, workloads.UPCONVERT])
+def test_single_request_prologue_edges(kind):
+    """The single-request prologue reads its three metadata values without a
+    branch: no seq_starts with a partial last page, a request whose first
+    output row is not 0, a start past the end of the table row, and a table
+    with no columns (never read; torch passes a null pointer for it)."""
+    mk = lambda name, **kw: workloads.make_workload(name, kind, [5000], 16, 576, 330, seed=77,
+                                                    scale=0.05, **kw)
+    check_parity(mk("single_no_starts_partial"), DEV)
+    wl = mk("single_offset_rows", workspace_rows=5000 + 40)
+    wl.cu_seq_lens = torch.tensor([23, 23 + 5000], dtype=torch.int32)
+    wl.num_tokens = 5000 + 23
+    check_parity(wl, DEV)
+    wl.num_tokens = 2000  # the extent clamps to the destination
+    check_parity(wl, DEV)
+    wl = mk("single_start_past_table", starts=[4000])
+    wl.block_table = wl.block_table[:, :100].contiguous()  # pages 250.. lie past the row
+    check_parity(wl, DEV)
+    wl = mk("single_empty_table")
+    wl.block_table = wl.block_table[:, :0].contiguous()
+    check_parity(wl, DEV)
+
+
+@pytest.mark.parametrize("R", [3, 100, 1500])
+def test_empty_block_table(R):
+    """A table with no columns on the batched paths (wave registers, LDS
+    prefix, prebuilt task table): every page is skipped, nothing is written."""
+    lens = [(37 * r) % 300 for r in range(R)]
+    wl = workloads.make_workload(f"empty_table_{R}", workloads.RAW, lens, 16, 64, sum(lens) // 16 + 2 * R,
+                                 seed=R)
+    wl.block_table = wl.block_table[:, :0].contiguous()
+    check_parity(wl, DEV)
+
+
 # ---------------------------------------------------------------------------
 # capture in a HIP graph: every replay recomputes from the current inputs
 # ---------------------------------------------------------------------------
