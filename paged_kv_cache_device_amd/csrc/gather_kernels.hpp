@@ -30,7 +30,10 @@
 //    scale, v_cvt_pk_bf16_f32 (round to nearest even);
 //  * every shape is a runtime argument; templates cover only the workgroup
 //    shape, the access width, and whether a page's rows are one contiguous
-//    span.
+//    span;
+//  * the fields the task lookup needs first are leading scalar kernel
+//    arguments, preloaded into SGPRs at wave start, so the metadata loads
+//    leave without waiting for a kernel-argument fetch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -90,7 +93,7 @@ struct GatherParams {
   const int32_t* cu_seq_lens;
   const int32_t* seq_starts;     // nullptr: every request starts at token 0
   const float* scale;            // fp8 only
-  const TaskRecord* tasks;       // nullptr: tasks are built in the kernel (LDS scan)
+  const TaskRecord* tasks;       // nullptr: tasks are found in the kernel (no prebuilt table)
   const int32_t* task_count;     // with tasks: device count of valid records
   int64_t src_block_stride;      // bytes
   int64_t src_token_stride;      // bytes
@@ -121,8 +124,9 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// n / d for n, d < 2^31 with a precomputed magic = ceil(2^32 / d) (d >= 2) or
-// 0xFFFFFFFF (d == 1): the multiply-high is off by at most one either way.
+// n / d for n < 2^32 and 1 <= d < 2^31, with a precomputed magic =
+// ceil(2^32 / d) (d >= 2) or 0xFFFFFFFF (d == 1).  The multiply-high is off by
+// at most one (too high for d >= 2, too low for d == 1); one step corrects it.
 __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t d, uint32_t magic) {
   uint32_t q = __umulhi(n, magic);
   const int32_t r = static_cast<int32_t>(n - q * d);
@@ -360,7 +364,8 @@ __device__ __forceinline__ Page page_from(const GatherParams& p, int64_t phys, i
 template <int K> struct CodesOf { using T = uint32_t; };
 template <> struct CodesOf<8> { using T = u32x2; };
 
-// K fp8 codes, read as one K-byte word when SRC_VEC (aligned) else byte by byte.
+// K fp8 codes, read as one K-byte word when SRC_VEC (code rows dword-aligned
+// for K >= 4, K-aligned below) else byte by byte.
 template <int K, bool SRC_VEC>
 __device__ __forceinline__ typename CodesOf<K>::T load_codes(const uint8_t* q) {
   if constexpr (SRC_VEC && K == 8) {
@@ -425,7 +430,7 @@ __device__ __forceinline__ typename OutOf<K>::T dequant_codes(typename CodesOf<K
 }
 
 // Where a page's source rows are read from.  fp8 code rows that are not
-// K-aligned (a 577-byte row pitch, say) are read as dword-aligned windows
+// dword-aligned (a 577-byte row pitch, say) are read as dword-aligned windows
 // around each lane's K codes, then shifted into place: one 12- or 8-byte load
 // instead of K byte loads.  A window is clamped to end at `lim`, the page's
 // used bytes rounded up to a whole dword, so no load touches a dword that
@@ -567,7 +572,7 @@ struct TaskSource {
   const int32_t* B;
   const int32_t* S;
   int32_t b, e, s;         // kSingle: the request's clamped extent and source start
-  int32_t first_phys_raw;  // kSingle: block-table entry of this workgroup's first task (raw)
+  int32_t first_phys_raw;  // kSingle: table entry of this workgroup's first task (-1 past the row)
 };
 
 // Resolve `task` (the same for every lane) to its page, all fields wave-uniform.
