@@ -23,6 +23,10 @@ def _declared_functions():
 def lib():
     from paged_kv_cache_device_amd import build
 
+    # another build of the same sources (the sanitizer test's host-only one)
+    other = os.environ.get("PKVG_TEST_LIBRARY")
+    if other:
+        return pkvg.library(other)
     if build.is_stale():
         build.build()
     return pkvg.library()
