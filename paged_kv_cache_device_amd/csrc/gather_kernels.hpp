@@ -585,30 +585,34 @@ __device__ __forceinline__ void load_batch(const GatherParams& p, const PageSrc&
 }
 
 // Stores of one batch.  Each store is guarded by its own lane's bound, except
-// on flat pages with the wide shape: there a wave whose lanes all have their U
-// chunks in range (every wave of a full page, whose chunk count is a multiple
-// of 64) waits for all its loads, converts every chunk, and issues its U
-// stores back to back; and 16-byte fp8 chunks of such pages go out as
-// device-scope (write-through) streaming stores.  Both were measured: they
-// shorten the 300K fp8 gather by 3% and the skew-8 raw one by 0.8%, and slow
-// the narrow-shape and strided gathers down, which keep the guarded stores.
+// on flat pages with the wide shape: there a wave whose lanes all have their
+// first U - 1 chunks in range (every wave of a full page: a page's chunk count
+// is a multiple of 64, so the wave's lanes agree on each chunk but the last)
+// waits for all its loads, converts every chunk, and issues those U - 1
+// stores back to back, then the last one under its lane guard; and 16-byte
+// fp8 chunks of such pages go out as device-scope (write-through) streaming
+// stores.  Both were measured: they shorten the 300K fp8 gather by 4% and the
+// skew-8 raw one by 1.5%, and slow the narrow-shape and strided gathers down,
+// which keep the guarded stores.
 template <class SH, class M>
 __device__ __forceinline__ void store_batch(const GatherParams& p, const PageDst& d, uint32_t n, uint32_t c0,
                                             const typename M::Reg (&r)[unroll_of<SH, M>()], float scale) {
   constexpr int U = unroll_of<SH, M>();
-  constexpr bool burst = SH::threads == Wide::threads && M::layout == kFlat;
+  constexpr bool burst = SH::threads == Wide::threads && M::layout == kFlat && U >= 2;
   constexpr bool write_through = burst && !M::is_copy && M::out_bytes == 16;
   if constexpr (burst) {
     // chunk c0 of the wave's last lane (wave-uniform): in range means every lane is
     const uint32_t wave_last = static_cast<uint32_t>(uniform(static_cast<int32_t>(c0 - (threadIdx.x & 63u)))) + 63u;
-    if (wave_last + (U - 1) * SH::threads < n) {
+    if (wave_last + (U - 2) * SH::threads < n) {
       typename M::Out o[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) o[u] = M::convert(r[u], scale);
       // a copy has no conversion to wait on: wait for all its loads here
       if constexpr (M::is_copy) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int u = 0; u < U; ++u) M::template store<write_through>(p, d, c0 + u * SH::threads, o[u]);
+      for (int u = 0; u < U - 1; ++u) M::template store<write_through>(p, d, c0 + u * SH::threads, o[u]);
+      const uint32_t c = c0 + (U - 1) * SH::threads;
+      if (c < n) M::template store<write_through>(p, d, c, o[U - 1]);
       return;
     }
   }
