@@ -76,7 +76,9 @@ int64_t max_bytes_stride(int64_t stride, int64_t elem) {
 }
 
 // Launches with at least this many page tasks (about four workgroups per CU)
-// use the wide workgroup shape; fewer use the narrow one.
+// use the wide workgroup shape; fewer use the narrow one, except fp8 pages
+// written as one contiguous span, which measured faster wide at any count
+// (they take the wide shape's store bursts and write-through stores).
 constexpr int64_t kWideMinTasks = 1024;
 
 // hipLaunchKernel returns the launch's own status, so the calling thread's
@@ -105,7 +107,8 @@ hipError_t launch_shape(const GatherParams& p, unsigned grid, size_t lds, hipStr
 
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  if (grid >= kWideMinTasks) return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  if (grid >= kWideMinTasks || (CONVERT == pkvg::kFp8Bf16 && LAYOUT == pkvg::kFlat))
+    return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
   return launch_shape<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
 }
 
