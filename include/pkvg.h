@@ -48,6 +48,9 @@
  *  - Calls are thread-safe and re-entrant.  Requests with more than
  *    PKVG_FUSED_MAX_REQS entries allocate a stream-ordered scratch buffer
  *    (hipMallocAsync / hipFreeAsync on `stream`); smaller ones allocate nothing.
+ *    A call enqueues kernel launches only (plus that allocation and its free)
+ *    and no memset, so it can be captured into a HIP graph; each replay reads
+ *    the buffers' contents at replay time.
  *  - Preconditions (not checked, out of contract): cu_seq_lens is
  *    non-decreasing with cu[0] >= 0; seq_starts >= 0; the source and
  *    destination do not overlap.

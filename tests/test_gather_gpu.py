@@ -10,7 +10,7 @@ import torch
 import oracle
 import oracle_pins
 import workloads
-from gpu_util import check_parity, log, run_hip
+from gpu_util import byte_diff, check_parity, log, run_hip
 
 pytestmark = pytest.mark.gpu
 
@@ -330,10 +330,11 @@ def test_empty_block_table(R):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("kind,R", [(workloads.RAW, 1), (workloads.UPCONVERT, 5),
-                                    (workloads.DEQUANT_FP8, 100)])
+                                    (workloads.DEQUANT_FP8, 100), (workloads.RAW, 1500)])
 def test_graph_replays(kind, R):
-    """The calls enqueue only kernel launches (no memset, no allocation up to
-    1024 requests), so they can be captured.  Between replays the cache
+    """The calls enqueue only kernel launches (up to 1024 requests) or kernel
+    launches between a stream-ordered allocation and its free (more requests),
+    and no memset, so they can be captured.  Between replays the cache
     contents change and eager work runs; each replay must match the oracle on
     the inputs of that moment."""
     import paged_kv_cache_device_amd as pkvg
@@ -418,3 +419,47 @@ def test_open_ended_cu_seq_lens(R, kind):
     n = int(count.item())
     assert n == len(tw)
     assert np.array_equal(tasks[:n].cpu().numpy()[:, :5], tw)
+
+
+# ---------------------------------------------------------------------------
+# calls from several host threads at once, each on its own stream
+# ---------------------------------------------------------------------------
+
+def test_concurrent_calls_from_threads():
+    """The library keeps no shared mutable state (its error slot is per thread):
+    eight threads, each on its own stream, run different gathers repeatedly
+    and every result matches the oracle."""
+    import threading
+
+    cases = []
+    for i, (kind, lens) in enumerate([(workloads.RAW, [700, 0, 33]), (workloads.UPCONVERT, [5000]),
+                                      (workloads.DEQUANT_FP8, [17] * 80), (workloads.RAW, [9] * 1200),
+                                      (workloads.RAW, [4096]), (workloads.UPCONVERT, [100, 200, 300]),
+                                      (workloads.DEQUANT_AUTO, [257, 64]), (workloads.DEQUANT_FP8, [31] * 1100)]):
+        wl = workloads.make_workload(f"threads_{i}", kind, lens, 16, 64, sum(-(-n // 16) for n in lens) + 3,
+                                     seed=500 + i, scale=0.05)
+        want, _ = oracle.run_workload(wl)
+        cases.append((wl.to(DEV), want))
+    errors = []
+
+    def worker(idx):
+        try:
+            d, want = cases[idx]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for _ in range(20):
+                    ws = d.fresh_workspace()
+                    run_hip(d, ws)
+                stream.synchronize()
+            if not torch.equal(ws.cpu().view(torch.uint8), want.view(torch.uint8)):
+                errors.append(f"case {idx}: " + byte_diff(ws.cpu(), want))
+        except Exception as e:  # reported below with the case that raised
+            errors.append(f"case {idx}: {e!r}")
+
+    log("[threads] 8 threads x 20 calls")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
