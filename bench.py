@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -30,7 +31,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
 METRIC = "effective HBM GB/s (read+write) and % of peak; median gather latency, 1 GPU"
 DEFAULT_WORKLOAD = "single_60k_raw"
 TRAFFIC_DIR = os.path.join(REPO, "profiles")
-KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp", "paged_kv_cache_device_amd/build.py",
+KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp",
                   "paged_kv_cache_device_amd/csrc/pkvg_capi.hip"]
 
 
@@ -38,11 +39,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed: edits that
+    cannot change the compiled code do not change the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Fingerprint of what the kernels are built from: the HIP sources (code
+    only) and the compiler flags."""
+    from paged_kv_cache_device_amd import build
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(REPO, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(REPO, rel)) as f:
+            h.update(_code_only(f.read()).encode())
+    h.update(repr(build.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

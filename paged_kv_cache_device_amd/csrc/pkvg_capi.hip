@@ -236,8 +236,9 @@ int plan_copy(Plan& pl, const void* src, void* dst, int64_t elem, int32_t entry,
   return PKVG_OK;
 }
 
-// fp8 -> bf16 plan: K codes per lane, limited by the bf16 store alignment (2K
-// bytes) and the row length; byte loads when the code rows are not K-aligned.
+// fp8 -> bf16 plan: K codes per lane, limited by the row length and the bf16
+// rows' alignment; code rows that are not dword-aligned are read as shifted
+// dword windows (K >= 4) or byte by byte (shorter rows, K < 4).
 int plan_fp8(Plan& pl, const void* src, void* dst, int32_t entry, int64_t sbs, int64_t sts,
              int64_t drs_elems, int32_t block_size) {
   const int64_t dr = max_bytes_stride(drs_elems, 2);
