@@ -264,6 +264,36 @@ def test_offsets_beyond_2_to_31_bytes():
     assert torch.equal(got.view(torch.int32), want.view(torch.int32))
 
 
+def test_fp8_offsets_beyond_2_to_31_bytes():
+    """The fp8 flat path (wide shape, write-through stores through a buffer
+    resource based at each page's first output row): 2,000,000 tokens of 576
+    codes write 2.3 GB of bf16, so page bases pass 2^31 bytes."""
+    import paged_kv_cache_device_amd as pkvg
+
+    T, bs, entry = 2_000_000, 64, 576
+    nb = T // bs + 1 + 40
+    log(f"[int64 fp8] T={T} output ~{T * entry * 2 / 2**30:.2f} GiB")
+    g = torch.Generator("cpu").manual_seed(65)
+    perm = torch.randperm(nb, generator=g).to(torch.int32)
+    pages = -(-T // bs)
+    bt = perm[:pages].view(1, pages).contiguous()
+    gd = torch.Generator(DEV).manual_seed(66)
+    codes = torch.randint(0, 256, (nb, bs, entry), dtype=torch.uint8, device=DEV, generator=gd)
+    codes[(codes & 0x7F) == 0x7F] -= 1  # no NaN codes
+    scale = torch.tensor([0.0625], dtype=torch.float32)
+    ws = torch.full((T + 2, entry), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    pkvg.gather_upconvert_fp8(codes, ws[:T], bt.to(DEV), cu.to(DEV), 1, scale.to(DEV), None)
+    torch.cuda.synchronize()
+    got = ws.cpu()
+    del ws
+    want = torch.full((T + 2, entry), -1, dtype=torch.int16).view(torch.bfloat16)
+    rows = oracle.load().gather_tensors(oracle.MODE_E4M3FN_TO_BF16, codes.cpu(), want[:T], bt, cu, None, 1,
+                                        float(scale[0]))
+    assert rows == T
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
 # ---------------------------------------------------------------------------
 # one request: the path that requests the first block-table entry early
 # ---------------------------------------------------------------------------
