@@ -132,6 +132,27 @@ def test_fp8_access_paths(kind, entry, ccols, dcols):
         check_parity(wl, DEV)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_wide_shape_random(seed):
+    """Random batches big enough for the wide workgroup shape (>= 1024 pages, or
+    any flat fp8 gather): block sizes whose pages have 64-multiple or ragged
+    chunk counts, entries of several widths, seq_starts, partial pages; the
+    wave-uniform store bursts and write-through stores against the oracle."""
+    g = torch.Generator("cpu").manual_seed(9000 + seed)
+    pick = lambda xs: xs[int(torch.randint(0, len(xs), (1,), generator=g))]
+    kind = pick([workloads.RAW, workloads.UPCONVERT, workloads.DEQUANT_FP8])
+    bs = pick([16, 32, 64, 128])
+    entry = pick([64, 136, 512, 576, 1000])
+    R = int(torch.randint(1, 9, (1,), generator=g))
+    target_pages = 1100 + int(torch.randint(0, 600, (1,), generator=g))
+    lens = [int(x) for x in torch.randint(1, 2 * target_pages * bs // R + 2, (R,), generator=g)]
+    starts = [int(torch.randint(0, n // 3 + 1, (1,), generator=g)) for n in lens]
+    pages = sum(-(-n // bs) for n in lens)
+    wl = workloads.make_workload(f"wide_rand_{seed}", kind, lens, bs, entry, pages + 5, seed=9100 + seed,
+                                 starts=starts, scale=0.05)
+    check_parity(wl, DEV)
+
+
 # ---------------------------------------------------------------------------
 # the fp8 arithmetic on every code, NaN codes included
 # ---------------------------------------------------------------------------
