@@ -126,6 +126,18 @@ def _device_i32(t: torch.Tensor | None, name: str, dim: int) -> torch.Tensor | N
     return t
 
 
+def _same_device(named) -> None:
+    """Every tensor on one device, and that device current: the library
+    launches on the current device's stream with the tensors' raw pointers."""
+    named = [(n, t) for n, t in named if t is not None]
+    dev = named[0][1].device
+    for n, t in named[1:]:
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, {named[0][0]} on {dev}")
+    if dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError(f"the tensors are on {dev}, the current device is cuda:{torch.cuda.current_device()}")
+
+
 def _terminal(cu_seq_lens: torch.Tensor, batch_size: int, cu_terminal) -> int:
     """1 when cu_seq_lens carries a terminal entry, 0 when the last request runs
     to num_tokens; by default decided by its length."""
@@ -157,6 +169,8 @@ def _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts
         raise ValueError("block_table needs batch_size rows")
     if seq_starts is not None and seq_starts.numel() < batch_size:
         raise ValueError("seq_starts needs batch_size entries")
+    _same_device([("dst", dst), ("src_cache", src_cache), ("block_table", block_table),
+                  ("cu_seq_lens", cu_seq_lens), ("seq_starts", seq_starts)])
     return [num_blocks, block_size, entry, src_cache.stride(0), src_cache.stride(1),
             _ptr(dst), dst.shape[0], dst.stride(0), _ptr(block_table), block_table.shape[1],
             block_table.stride(0), _ptr(cu_seq_lens), terminal, _ptr(seq_starts), batch_size]
@@ -194,11 +208,13 @@ def _fp8_source(src_cache: torch.Tensor) -> None:
         raise TypeError(f"an fp8 cache must be uint8 or float8_e4m3fn, got {src_cache.dtype}")
 
 
-def _scale_tensor(scale) -> torch.Tensor:
+def _scale_tensor(scale, dst: torch.Tensor) -> torch.Tensor:
     if not isinstance(scale, torch.Tensor) or scale.dtype != torch.float32 or not scale.is_cuda:
         raise TypeError("scale must be a float32 device tensor with one element")
     if scale.numel() < 1:
         raise ValueError("scale must hold one element")
+    if scale.device != dst.device:
+        raise ValueError(f"scale is on {scale.device}, dst on {dst.device}")
     return scale
 
 
@@ -212,7 +228,7 @@ def _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size,
         code, sc = PKVG_KV_AUTO, None
     elif kv_cache_dtype in ("fp8", "fp8_e4m3"):
         _fp8_source(src_cache)
-        code, sc = PKVG_KV_FP8_E4M3, _scale_tensor(scale)
+        code, sc = PKVG_KV_FP8_E4M3, _scale_tensor(scale, dst)
     else:
         raise ValueError(f"unknown kv_cache_dtype {kv_cache_dtype!r}")
     args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts,
@@ -226,7 +242,7 @@ def _prepare_upconvert(src_cache, dst, block_table, cu_seq_lens, batch_size, sca
     if dst.dtype != torch.bfloat16:
         raise TypeError("gather_upconvert_fp8 writes a bf16 destination")
     _fp8_source(src_cache)
-    sc = _scale_tensor(scale)
+    sc = _scale_tensor(scale, dst)
     args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts,
                        cu_terminal)
     return PreparedCall("gather_upconvert_fp8", [_ptr(src_cache), *args, _ptr(sc),
@@ -286,6 +302,7 @@ def gather_page_tasks(cu_seq_lens: torch.Tensor, seq_starts: torch.Tensor | None
     _device_i32(block_table, "block_table", 2)
     _device_i32(cu_seq_lens, "cu_seq_lens", 1)
     _device_i32(seq_starts, "seq_starts", 1)
+    _same_device([("cu_seq_lens", cu_seq_lens), ("block_table", block_table), ("seq_starts", seq_starts)])
     if capacity is None:
         capacity = num_tokens // block_size + 2 * batch_size + 1
     dev = cu_seq_lens.device
