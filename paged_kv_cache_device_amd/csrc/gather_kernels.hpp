@@ -47,9 +47,10 @@ namespace pkvg {
 // A narrow batch (256 lanes x 288 bytes = 72 KiB of output) holds a whole
 // 64-token page of 1152-byte rows, so all of a page's loads are in flight at
 // once; the wide shape (1024 x 80 bytes) does the same with four times the
-// waves per workgroup.  Few pages (one wave of workgroups over the chip) run
-// best narrow, many pages wide.  Chunks per lane per batch follow from the
-// chunk's output size (see unroll_of).
+// waves per workgroup.  Smaller pages take shapes sized to them (mid: 36 KiB,
+// small: 20 KiB), so more of them fit on a CU at once and each workgroup's
+// metadata round trip hides behind other pages' data.  Chunks per lane per
+// batch follow from the chunk's output size (see unroll_of).
 template <int NT, int LANE_BYTES>
 struct Shape {
   static constexpr int threads = NT;
@@ -58,6 +59,8 @@ struct Shape {
 };
 using Narrow = Shape<256, 288>;
 using Wide = Shape<1024, 80>;
+using Mid = Shape<256, 144>;
+using Small = Shape<256, 80>;
 
 constexpr int kScanThreads = 1024;
 
@@ -241,33 +244,52 @@ struct Page {
   int32_t rows;      // rows to copy (<= 0: nothing)
 };
 
+// Batches of at most this many requests find their tasks inside the gather
+// kernel (wave registers or an LDS prefix); larger ones use a prebuilt table.
+constexpr int kFusedMaxReqs = 1024;
+
 // Fill the LDS task prefix for the fused path: P[0..R] exclusive prefix of page
 // counts, B[0..R] clamped output begins (B[R] = clamped end of the last
-// request), S[0..R) source starts.  Every thread of the workgroup takes part.
+// request), S[0..R) source starts.  Every thread of the workgroup takes part:
+// thread t owns requests [t * PER, t * PER + PER) and issues all its loads
+// (PER + 1 cu_seq_lens entries, PER starts) before using any of them, so the
+// prefix costs one memory round trip.
 template <int NT>
 __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t* P, int32_t* B,
                                                  int32_t* S, int32_t* scan_tmp) {
+  constexpr int PER = (kFusedMaxReqs + NT - 1) / NT;
   const int32_t R = p.num_reqs;
-  const int32_t per = (R + NT - 1) / NT;
-  const int32_t lo = min(static_cast<int32_t>(threadIdx.x) * per, R);
-  const int32_t hi = min(lo + per, R);
+  const int32_t ncu = R + p.cu_terminal;  // entries of cu_seq_lens
+  const int32_t lo = static_cast<int32_t>(threadIdx.x) * PER;
+  // cu[lo + k], or num_tokens past the array: request r ends at entry r + 1
+  int64_t cuv[PER + 1];
+  int32_t st[PER];
+#pragma unroll
+  for (int k = 0; k <= PER; ++k) cuv[k] = lo + k < ncu ? p.cu_seq_lens[lo + k] : p.num_tokens;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) st[k] = (p.seq_starts != nullptr && lo + k < R) ? p.seq_starts[lo + k] : 0;
+  int32_t cnt[PER];
   int32_t sum = 0;
-  for (int32_t r = lo; r < hi; ++r) {
-    const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
-    const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
-    const int32_t s = p.seq_starts ? p.seq_starts[r] : 0;
-    const int32_t c = page_count(p, b, e, s);
-    B[r] = static_cast<int32_t>(b);
-    S[r] = s;
-    P[r] = c;
-    sum += c;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    cnt[k] = 0;
+    if (lo + k < R) {
+      const int64_t b = clamp_rows(cuv[k], p.num_tokens);
+      const int64_t e = clamp_rows(cuv[k + 1], p.num_tokens);
+      cnt[k] = page_count(p, b, e, st[k]);
+      B[lo + k] = static_cast<int32_t>(b);
+      S[lo + k] = st[k];
+      sum += cnt[k];
+    }
   }
   int32_t total;
   int32_t off = block_exclusive_scan<NT>(sum, scan_tmp, total);
-  for (int32_t r = lo; r < hi; ++r) {
-    const int32_t c = P[r];
-    P[r] = off;
-    off += c;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (lo + k < R) {
+      P[lo + k] = off;
+      off += cnt[k];
+    }
   }
   if (threadIdx.x == 0) {
     P[R] = total;

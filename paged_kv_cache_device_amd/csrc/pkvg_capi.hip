@@ -15,6 +15,8 @@ namespace {
 using pkvg::GatherParams;
 using pkvg::TaskRecord;
 
+static_assert(pkvg::kFusedMaxReqs == PKVG_FUSED_MAX_REQS, "the fused task paths cover the header's batch limit");
+
 thread_local int g_last_hip_error = 0;
 
 // Workgroups launched: one per task up to this cap; any grid is correct
@@ -75,11 +77,21 @@ int64_t max_bytes_stride(int64_t stride, int64_t elem) {
   return stride > INT64_MAX / elem ? -1 : stride * elem;
 }
 
-// Launches with at least this many page tasks (about four workgroups per CU)
-// use the wide workgroup shape; fewer use the narrow one, except fp8 pages
-// written as one contiguous span, which measured faster wide at any count
-// (they take the wide shape's store bursts and write-through stores).
+// Workgroup shape by page size and batch (each choice measured):
+//  * pages of at most 20 KiB of output take the small shape, of at most 36 KiB
+//    the mid one: sized to the page, they fit more pages per CU (2.0-2.5x on
+//    16- and 32-token pages);
+//  * larger pages take the wide shape when the batch is found in wave
+//    registers or is one request (at most 64 requests) and there are at least
+//    this many page tasks (about four workgroups per CU), or the pages are fp8
+//    written as one contiguous span (they take the wide shape's store bursts
+//    and write-through stores);
+//  * otherwise the narrow shape (fewer pages, or batches of more than 64
+//    requests, whose per-workgroup prefix build hides better behind more,
+//    smaller workgroups).
 constexpr int64_t kWideMinTasks = 1024;
+constexpr int64_t kSmallMaxPageBytes = 20 * 1024;
+constexpr int64_t kMidMaxPageBytes = 36 * 1024;
 
 // hipLaunchKernel returns the launch's own status, so the calling thread's
 // error state (which other libraries use) is neither read nor cleared.
@@ -107,7 +119,12 @@ hipError_t launch_shape(const GatherParams& p, unsigned grid, size_t lds, hipStr
 
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  if (grid >= kWideMinTasks || (CONVERT == pkvg::kFp8Bf16 && LAYOUT == pkvg::kFlat))
+  const int64_t page_out = int64_t(p.block_size) * p.row_in_bytes * (CONVERT == pkvg::kFp8Bf16 ? 2 : 1);
+  if (page_out <= kSmallMaxPageBytes)
+    return launch_shape<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  if (page_out <= kMidMaxPageBytes) return launch_shape<pkvg::Mid, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  if (p.num_reqs <= pkvg::kWaveMaxReqs &&
+      (grid >= kWideMinTasks || (CONVERT == pkvg::kFp8Bf16 && LAYOUT == pkvg::kFlat)))
     return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
   return launch_shape<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
 }
