@@ -153,6 +153,47 @@ def test_wide_shape_random(seed):
     check_parity(wl, DEV)
 
 
+def medium_random_workload(seed: int) -> workloads.Workload:
+    """A seeded mid-size batch: every workgroup shape (page sizes from a few KiB
+    to over 72 KiB), every task path (one request, wave registers, LDS prefix,
+    task table), raw widths and fp8 code widths, strided rows, seq_starts,
+    aliased blocks, guard-skipped pages, clamped and open-ended extents."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    kind = [workloads.RAW, workloads.DEQUANT_FP8, workloads.UPCONVERT, workloads.DEQUANT_AUTO][seed % 4]
+    R = [1, 3, 20, 64, 65, 200, 1100][ri(0, 6)]
+    bs = [8, 16, 32, 64, 128][ri(0, 4)]
+    entry = [64, 136, 256, 512, 576, 1000][ri(0, 5)]
+    cache_dtype = [torch.bfloat16, torch.float32, torch.uint8][ri(0, 2)]
+    max_tokens = max(40_000 // R, 2)
+    lens = [0 if ri(0, 9) == 0 else ri(1, max_tokens) for _ in range(R)]
+    starts = [ri(0, n // 2) for n in lens] if ri(0, 1) else None
+    pages = sum(-(-n // bs) for n in lens)
+    alias = ri(0, 3) == 0
+    nb = max(pages, 1) + ri(0, 8) if not alias else max([-(-n // bs) for n in lens] + [1]) + 2
+    wl = workloads.make_workload(f"medium_{seed}", kind, lens, bs, entry, nb, seed=seed + 77,
+                                 starts=starts, cache_cols=entry + [0, 0, 1, 4][ri(0, 3)],
+                                 dst_cols=entry + [0, 0, 2, 4][ri(0, 3)], scale=[0.0625, 0.05][ri(0, 1)],
+                                 allow_alias=alias, cache_dtype=cache_dtype)
+    total = int(wl.cu_seq_lens[-1])
+    if ri(0, 4) == 0 and total > 0:
+        T = ri(0, total)
+        wl.num_tokens = T
+        wl.workspace = wl.workspace[: max(T, 1)].clone()
+    if ri(0, 4) == 0:
+        wl = wl.open_ended()
+    if ri(0, 2) == 0 and wl.block_table.numel() > 0:
+        flat = wl.block_table.view(-1)
+        for _ in range(ri(1, 5)):
+            flat[ri(0, flat.numel() - 1)] = [nb, nb + 9, -1][ri(0, 2)]
+    return wl
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_medium_random(seed):
+    check_parity(medium_random_workload(seed), DEV)
+
+
 # ---------------------------------------------------------------------------
 # the fp8 arithmetic on every code, NaN codes included
 # ---------------------------------------------------------------------------
