@@ -306,6 +306,15 @@ def mixed_dequant_strided() -> Workload:
                          workspace_rows=sum(lens) + 16)
 
 
+def batch_raw(R: int, bs: int, seed: int, kind: str = RAW) -> Workload:
+    """R requests of 12,800 / bs tokens each (800 at bs 16, 400 at bs 32, 200 at
+    bs 64: 50, 12.5 and 3.1 pages per request), entry 576, shuffled blocks.  Not a scenario of the pages: batches of many requests
+    on small pages, used to choose the workgroup shape by page size."""
+    n = 12800 // bs
+    name = f"batch{R}_bs{bs}_{'fp8' if kind in FP8_KINDS else 'raw'}"
+    return make_workload(name, kind, [n] * R, bs, 576, R * (-(-n // bs)) + 8, seed=seed, scale=0.0625)
+
+
 NAMED = {
     "tiny_raw": tiny_raw,
     "single_60k_raw": single_60k_raw,
@@ -314,6 +323,11 @@ NAMED = {
     "skew2_raw_seq_starts": skew2_raw_starts,
     "skew4_raw_seq_starts": skew4_raw_starts,
     "mixed_fp8_dequant_strided": mixed_dequant_strided,
+    "batch512_bs16_raw": lambda: batch_raw(512, 16, 1101),
+    "batch512_bs16_fp8": lambda: batch_raw(512, 16, 1102, UPCONVERT),
+    "batch512_bs32_raw": lambda: batch_raw(512, 32, 1103),
+    "batch512_bs64_raw": lambda: batch_raw(512, 64, 1104),
+    "batch512_bs64_fp8": lambda: batch_raw(512, 64, 1105, UPCONVERT),
 }
 
 
