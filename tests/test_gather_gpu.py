@@ -213,13 +213,20 @@ def test_fp8_every_code(scale):
     dst = torch.full((4, 64), -1, dtype=torch.int16).view(torch.bfloat16)
     o = oracle.load()
     want = torch.tensor([o.dequant_e4m3fn_bf16(c, scale) for c in range(256)], dtype=torch.int32)
-    d = dst.to(DEV)
-    pkvg.gather_upconvert_fp8(codes.to(DEV), d, bt.to(DEV), cu.to(DEV), 1, sc.to(DEV))
-    torch.cuda.synchronize()
-    got = d.cpu().view(torch.int16).flatten().to(torch.int32) & 0xFFFF
     nan = torch.tensor([c in (0x7F, 0xFF) for c in range(256)])
-    assert torch.equal(got[~nan], want[~nan]), (got[~nan] != want[~nan]).nonzero().flatten()[:8]
-    assert torch.isnan(d.cpu().flatten().float()[nan]).all()
+    # the cache as raw bytes and as torch's float8_e4m3fn (same bits), through both fp8 calls
+    for cache in (codes.to(DEV), codes.to(DEV).view(torch.float8_e4m3fn)):
+        for call in ("upconvert", "maybe_dequant"):
+            d = dst.to(DEV)
+            if call == "upconvert":
+                pkvg.gather_upconvert_fp8(cache, d, bt.to(DEV), cu.to(DEV), 1, sc.to(DEV))
+            else:
+                pkvg.gather_maybe_dequant(cache, d, bt.to(DEV), cu.to(DEV), 1, "fp8", sc.to(DEV))
+            torch.cuda.synchronize()
+            got = d.cpu().view(torch.int16).flatten().to(torch.int32) & 0xFFFF
+            assert torch.equal(got[~nan], want[~nan]), (call, cache.dtype,
+                                                        (got[~nan] != want[~nan]).nonzero().flatten()[:8])
+            assert torch.isnan(d.cpu().flatten().float()[nan]).all()
 
 
 # ---------------------------------------------------------------------------
