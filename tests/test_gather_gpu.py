@@ -153,6 +153,23 @@ def test_wide_shape_random(seed):
     check_parity(wl, DEV)
 
 
+@pytest.mark.parametrize("bs,lens,kind", [
+    (1024, [20000], workloads.RAW),
+    (1024, [20000], workloads.UPCONVERT),
+    (4096, [9000, 0, 17, 5000], workloads.RAW),
+    (4096, [9000, 4097], workloads.DEQUANT_FP8),
+    (2048, [3000] * 70, workloads.RAW),
+])
+def test_large_pages(bs, lens, kind):
+    """Pages of 1,024-4,096 tokens (1.2-4.7 MB of output each): every workgroup
+    moves its page in several batches, with seq_starts and partial pages."""
+    starts = [n // 3 for n in lens]
+    pages = sum(-(-n // bs) for n in lens)
+    wl = workloads.make_workload(f"large_pages_{bs}_{kind}_{len(lens)}", kind, lens, bs, 576, pages + 3,
+                                 seed=bs + len(lens), starts=starts, scale=0.05)
+    check_parity(wl, DEV)
+
+
 def medium_random_workload(seed: int) -> workloads.Workload:
     """A seeded mid-size batch: every workgroup shape (page sizes from a few KiB
     to over 72 KiB), every task path (one request, wave registers, LDS prefix,
