@@ -28,6 +28,11 @@
 //  * fp8 pages: each lane reads 8 codes (8 bytes) and writes 8 bf16 (16
 //    bytes): v_cvt_pk_f32_fp8 (OCP e4m3fn on gfx950), one v_mul_f32 by the
 //    scale, v_cvt_pk_bf16_f32 (round to nearest even);
+//  * a task is normally one logical page; pages far larger than one
+//    workgroup batch are split into 2^k equal parts (each its own task), and
+//    pages of one to a few tokens are moved by a second kernel whose task is
+//    a group of 2^k consecutive pages, so page sizes from 1 to thousands of
+//    tokens all keep the chip busy;
 //  * every shape is a runtime argument; templates cover only the workgroup
 //    shape, the access width, and whether a page's rows are one contiguous
 //    span;
@@ -106,13 +111,17 @@ struct GatherParams {
   int64_t num_tokens;
   int32_t num_reqs;
   int32_t cu_terminal;           // 1: cu_seq_lens has num_reqs + 1 entries; 0: the last request ends at num_tokens
-  int32_t block_size;
+  int32_t task_tokens;           // tokens per task: block_size >> split_shift
+  int32_t split_shift;           // a page is 2^split_shift tasks (large pages); 0: one task per page
   int32_t block_table_width;
   int32_t chunks_per_row;        // row chunks (kRows), or chunks per row of the flat span (kFlat)
   int32_t row_in_bytes;          // bytes of a source row that are gathered
   uint32_t chunks_magic;         // ceil(2^32 / chunks_per_row), or 0xFFFFFFFF for 1
-  uint32_t block_size_magic;     // ceil(2^32 / block_size), or 0xFFFFFFFF for 1
+  uint32_t task_tokens_magic;    // ceil(2^32 / task_tokens), or 0xFFFFFFFF for 1
   int32_t task_capacity;         // with tasks: records available
+  int32_t group_shift;           // group kernel: a task is 2^group_shift consecutive pages (small pages)
+  int32_t page_tokens;           // group kernel: block_size
+  uint32_t page_tokens_magic;    // group kernel: ceil(2^32 / block_size), or 0xFFFFFFFF for 1
 };
 
 // ---------------------------------------------------------------------------
@@ -181,16 +190,19 @@ template <> struct VecOf<4> { using T = uint32_t; };
 template <> struct VecOf<2> { using T = uint16_t; };
 template <> struct VecOf<1> { using T = uint8_t; };
 
-// Token index -> logical page: floor(t / block_size) for 0 <= t < 2^32, a
+// Token index -> task unit: floor(t / task_tokens) for 0 <= t < 2^32, a
 // multiply-high instead of a 64-bit division.  Token indices stay below 2^32:
-// a request starts below 2^31 and gathers fewer than 2^31 rows.
+// a request starts below 2^31 and gathers fewer than 2^31 rows.  A task unit
+// is a logical page, or with split_shift > 0 one of the 2^split_shift equal
+// parts of a page, so that a few very large pages still spread over many
+// workgroups.
 __device__ __forceinline__ uint32_t page_of(const GatherParams& p, int64_t t) {
-  return div_magic(static_cast<uint32_t>(t), static_cast<uint32_t>(p.block_size), p.block_size_magic);
+  return div_magic(static_cast<uint32_t>(t), static_cast<uint32_t>(p.task_tokens), p.task_tokens_magic);
 }
 
-// Page counts of one request: rows [b, e) of the output, source tokens from s,
-// i.e. the pages holding tokens s .. s + (e - b) - 1.  A request with no rows
-// has no pages.
+// Task counts of one request: rows [b, e) of the output, source tokens from s,
+// i.e. the task units holding tokens s .. s + (e - b) - 1.  A request with no
+// rows has no tasks.
 __device__ __forceinline__ int32_t page_count(const GatherParams& p, int64_t b, int64_t e, int64_t s) {
   const int64_t n = e - b;
   if (n <= 0) return 0;
@@ -359,16 +371,18 @@ struct TaskGeom {
 
 __device__ __forceinline__ TaskGeom task_geometry(const GatherParams& p, int32_t j, int64_t b, int64_t e,
                                                   int64_t s) {
-  const int32_t bs = p.block_size;
+  const int32_t tt = p.task_tokens;
   const int64_t n = e - b > 0 ? e - b : 0;
-  const int64_t logical = static_cast<int64_t>(page_of(p, s)) + j;
-  const int64_t page0 = logical * bs;
-  const int64_t cb = s > page0 ? s : page0;
-  const int64_t ce = (s + n) < (page0 + bs) ? (s + n) : (page0 + bs);
+  const int64_t unit = static_cast<int64_t>(page_of(p, s)) + j;
+  const int64_t unit0 = unit * tt;
+  const int64_t cb = s > unit0 ? s : unit0;
+  const int64_t ce = (s + n) < (unit0 + tt) ? (s + n) : (unit0 + tt);
+  // the unit's first slot inside its page
+  const int32_t sub = static_cast<int32_t>(unit & ((int64_t(1) << p.split_shift) - 1)) * tt;
   TaskGeom g;
-  g.logical = static_cast<int32_t>(logical);
-  g.pbeg = static_cast<int32_t>(cb - page0);
-  g.pend = static_cast<int32_t>(ce - page0);
+  g.logical = static_cast<int32_t>(unit >> p.split_shift);
+  g.pbeg = static_cast<int32_t>(cb - unit0) + sub;
+  g.pend = static_cast<int32_t>(ce - unit0) + sub;
   g.out_begin = b + (cb - s);
   return g;
 }
@@ -723,23 +737,25 @@ __device__ __forceinline__ int32_t load_i32_vector_path(const int32_t* q) {
 // 64 < num_reqs): (3 * num_reqs + 2) int32.
 //
 // The leading scalar arguments repeat the fields of `params` that the task
-// lookup needs first, and `mode` is the TaskMode the host chose.  Leading
+// lookup needs first; `mode_and_split` holds the TaskMode the host chose (low
+// byte) and split_shift (the byte above it).  Leading
 // scalars are preloaded into SGPRs when a wave starts (gfx950 kernarg
 // preloading), so the metadata loads go out without waiting for a kernel
 // argument fetch; the struct arrives while they are in flight.
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
-    const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts, int32_t mode,
-    int32_t num_reqs, int32_t block_size, uint32_t block_size_magic, int32_t block_table_width,
-    int32_t cu_terminal, int64_t num_tokens, GatherParams params) {
+    const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
+    int32_t mode_and_split, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
+    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, GatherParams params) {
   using M = Mover<CONVERT, W, LAYOUT, SRC_VEC>;
   GatherParams p = params;
   p.cu_seq_lens = cu_seq_lens;
   p.block_table = block_table;
   p.seq_starts = seq_starts;
   p.num_reqs = num_reqs;
-  p.block_size = block_size;
-  p.block_size_magic = block_size_magic;
+  p.task_tokens = task_tokens;
+  p.task_tokens_magic = task_tokens_magic;
+  p.split_shift = mode_and_split >> 8;
   p.block_table_width = block_table_width;
   p.cu_terminal = cu_terminal;
   p.num_tokens = num_tokens;
@@ -748,7 +764,7 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
 
   const int32_t R = p.num_reqs;
   TaskSource ts;
-  ts.mode = mode;
+  ts.mode = mode_and_split & 0xFF;
   int32_t* P = lds;
   int32_t* B = lds + (R + 1);
   int32_t* S = lds + 2 * (R + 1);
@@ -758,14 +774,15 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
 
   int32_t num_tasks;
   if (ts.mode == kSingle) {
-    // The first page's logical block is seq_start / block_size + blockIdx.x:
-    // its block-table entry is requested together with the request extent
-    // instead of after it (one dependent memory round trip less).  Every load
-    // here is unconditional (an always-valid address stands in for an absent
-    // one) and the start goes through the vector path, so without seq_starts
-    // nothing waits before the entry and the extent are requested.
+    // The first task's logical block is (seq_start / task_tokens + blockIdx.x)
+    // >> split_shift: its block-table entry is requested together with the
+    // request extent instead of after it (one dependent memory round trip
+    // less).  Every load here is unconditional (an always-valid address stands
+    // in for an absent one) and the start goes through the vector path, so
+    // without seq_starts nothing waits before the entry and the extent are
+    // requested.
     ts.s = p.seq_starts ? load_i32_vector_path(p.seq_starts) : 0;
-    const uint32_t lb0 = page_of(p, ts.s) + blockIdx.x;
+    const uint32_t lb0 = (page_of(p, ts.s) + blockIdx.x) >> p.split_shift;
     const bool in_row = lb0 < static_cast<uint32_t>(p.block_table_width);
     const int32_t* entry_at = in_row ? p.block_table + lb0 : p.cu_seq_lens;
     const int32_t* end_at = p.cu_seq_lens + p.cu_terminal;  // cu_terminal is 0 or 1
@@ -804,6 +821,203 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
     const uint32_t n = static_cast<uint32_t>(pg.rows) * cpr;
     move_page<SH, M>(p, page_src(p.src + uniform64(pg.src_off), used),
                      page_dst(p.dst + uniform64(pg.dst_off), n * M::out_bytes), n, scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// page groups: pages of a few tokens
+// ---------------------------------------------------------------------------
+
+// A page of one to a few rows is too little work for a workgroup of its own:
+// the metadata round trips, not the data, would set the pace.  The group
+// kernel's task is instead G = 2^group_shift consecutive logical pages of one
+// request (task_tokens = G * block_size), whose rows are contiguous in the
+// output but scattered in the cache.  Each wave looks the group's G pages up
+// once (lane i holds page i's source offset, -1 when a guard skips it), and
+// every chunk fetches its row's page offset from that lane with a cross-lane
+// read.
+
+struct GroupTask {
+  int32_t req;
+  int32_t unit;       // group index within the request's logical pages
+  int32_t gbeg;       // first token copied, relative to the group's first token
+  int32_t gend;
+  int64_t out_begin;  // first output row
+};
+
+__device__ __forceinline__ GroupTask group_from(int32_t r, const TaskGeom& g) {
+  GroupTask t;
+  t.req = r;
+  t.unit = g.logical;
+  t.gbeg = g.pbeg;
+  t.gend = g.pend;
+  t.out_begin = g.out_begin;
+  return t;
+}
+
+// `task` -> its group, all fields wave-uniform (task geometry with split_shift 0
+// and task_tokens = G * block_size gives group-relative token ranges).
+__device__ __forceinline__ GroupTask resolve_group(const GatherParams& p, const TaskSource& ts, int32_t task) {
+  if (ts.mode == kSingle) return group_from(0, task_geometry(p, task, ts.b, ts.e, ts.s));
+  if (ts.mode == kWaveRegs) {
+    const int32_t r = uniform(static_cast<int32_t>(__popcll(__ballot(ts.wp.incl <= task))));
+    const int32_t b = uniform(__builtin_amdgcn_readlane(ts.wp.b, r));
+    const int32_t e = uniform(__builtin_amdgcn_readlane(ts.wp.e, r));
+    const int32_t s = uniform(__builtin_amdgcn_readlane(ts.wp.s, r));
+    const int32_t first = uniform(__builtin_amdgcn_readlane(ts.wp.incl - ts.wp.count, r));
+    return group_from(r, task_geometry(p, task - first, b, e, s));
+  }
+  if (ts.mode == kLdsPrefix) {
+    const int32_t r = uniform(find_request(ts.P, p.num_reqs, task));
+    return group_from(r, task_geometry(p, task - uniform(ts.P[r]), uniform(ts.B[r]), uniform(ts.B[r + 1]),
+                                       uniform(ts.S[r])));
+  }
+  const TaskRecord rec = p.tasks[task];
+  GroupTask t;
+  t.req = uniform(rec.req);
+  t.unit = uniform(rec.logical);
+  t.gbeg = uniform(rec.page_begin);
+  t.gend = uniform(rec.page_end);
+  t.out_begin = uniform(rec.out_begin);
+  return t;
+}
+
+// One batch of a group: U chunks per lane, chunk c = row c / cpr (row gbeg + c / cpr
+// of the group), column c % cpr.  `lane_phys` is this lane's page of the group
+// (lane < G), -1 when a guard skips it.  Every chunk first finds its row and
+// page, then all chunks fetch their page's block with cross-lane reads, then
+// all loads go out: the phases keep the cross-lane reads from serialising the
+// loads.  As in the page kernel, a lane past the end re-reads the last chunk
+// and skips its store, and rows of skipped pages read block 0 (it exists
+// whenever some page of the group is valid) and store nothing.
+template <class SH, class M, int LAYOUT>
+__device__ __forceinline__ void move_group(const GatherParams& p, int32_t lane_phys, uint32_t gbeg, uint32_t n,
+                                           uint8_t* dst_first, float scale) {
+  constexpr int U = unroll_of<SH, M>();
+  const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
+  const uint32_t bs = static_cast<uint32_t>(p.page_tokens);
+  for (uint32_t c0 = threadIdx.x; c0 - threadIdx.x < n; c0 += SH::threads * U) {
+    uint32_t row[U], col[U], k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = min(c0 + u * SH::threads, n - 1);
+      row[u] = div_magic(c, cpr, p.chunks_magic);
+      col[u] = c - row[u] * cpr;
+      k[u] = div_magic(gbeg + row[u], bs, p.page_tokens_magic);
+    }
+    int32_t phys[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) phys[u] = __shfl(lane_phys, static_cast<int>(k[u]), 64);
+    typename M::Reg r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t slot = gbeg + row[u] - k[u] * bs;
+      const int64_t base = static_cast<int64_t>(phys[u] < 0 ? 0 : phys[u]) * p.src_block_stride;
+      const uint8_t* rowp = p.src + base + slot * static_cast<uint32_t>(p.src_token_stride);
+      M::load(p, page_src(rowp, static_cast<uint32_t>(p.row_in_bytes)), col[u], r[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = c0 + u * SH::threads;
+      if (phys[u] < 0 || c >= n) continue;
+      uint8_t* q;
+      if constexpr (LAYOUT == kFlat) {
+        q = dst_first + c * M::out_bytes;
+      } else {
+        q = dst_first + row[u] * p.dst_row_stride + col[u] * M::out_bytes;
+      }
+      store_stream(q, M::convert(r[u], scale));
+    }
+  }
+}
+
+// The group kernel: the page kernel's task lookup with task_tokens = G *
+// block_size, then per-lane page lookups and move_group.  Same leading
+// arguments; `mode_and_group` holds the TaskMode (low byte) and group_shift
+// (the byte above it).  Loads always use flat (row-relative) chunk addressing:
+// each row is addressed on its own.
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+__global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
+    const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
+    int32_t mode_and_group, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
+    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, GatherParams params) {
+  using M = Mover<CONVERT, W, kFlat, SRC_VEC>;
+  GatherParams p = params;
+  p.cu_seq_lens = cu_seq_lens;
+  p.block_table = block_table;
+  p.seq_starts = seq_starts;
+  p.num_reqs = num_reqs;
+  p.task_tokens = task_tokens;
+  p.task_tokens_magic = task_tokens_magic;
+  p.block_table_width = block_table_width;
+  p.cu_terminal = cu_terminal;
+  p.num_tokens = num_tokens;
+  p.split_shift = 0;
+  p.group_shift = mode_and_group >> 8;
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t scan_tmp[SH::waves];
+
+  const int lane = threadIdx.x & 63;
+  const int32_t G = 1 << p.group_shift;
+  const int32_t R = p.num_reqs;
+  TaskSource ts;
+  ts.mode = mode_and_group & 0xFF;
+  int32_t* P = lds;
+  int32_t* B = lds + (R + 1);
+  int32_t* S = lds + 2 * (R + 1);
+  ts.P = P;
+  ts.B = B;
+  ts.S = S;
+
+  int32_t num_tasks;
+  if (ts.mode == kSingle) {
+    // as in the page kernel: this workgroup's first group's table entries
+    // (one per lane) are requested together with the request extent
+    ts.s = p.seq_starts ? load_i32_vector_path(p.seq_starts) : 0;
+    const int64_t lp = (static_cast<int64_t>(page_of(p, ts.s) + blockIdx.x) << p.group_shift) + lane;
+    const bool in_row = lane < G && lp < p.block_table_width;
+    const int32_t* entry_at = in_row ? p.block_table + lp : p.cu_seq_lens;
+    const int32_t* end_at = p.cu_seq_lens + p.cu_terminal;
+    const int32_t raw = *entry_at;
+    const int32_t cb = uniform(p.cu_seq_lens[0]);
+    const int32_t ce = uniform(*end_at);
+    ts.first_phys_raw = in_row ? raw : -1;
+    ts.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
+    ts.e = static_cast<int32_t>(clamp_rows(p.cu_terminal ? ce : p.num_tokens, p.num_tokens));
+    num_tasks = page_count(p, ts.b, ts.e, ts.s);
+  } else if (ts.mode == kWaveRegs) {
+    ts.wp = build_prefix_wave(p);
+    num_tasks = ts.wp.total;
+  } else if (ts.mode == kLdsPrefix) {
+    build_prefix_lds<SH::threads>(p, P, B, S, scan_tmp);
+    num_tasks = P[R];
+  } else {
+    num_tasks = min(*p.task_count, p.task_capacity);
+  }
+  num_tasks = uniform(num_tasks);
+  float scale = 1.0f;
+  if constexpr (CONVERT == kFp8Bf16)
+    scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*p.scale)));
+
+  const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
+  for (int32_t task = blockIdx.x; task < num_tasks; task += gridDim.x) {
+    const GroupTask t = resolve_group(p, ts, task);
+    const int32_t rows = t.gend - t.gbeg;
+    if (rows <= 0) continue;
+    int64_t phys = -1;
+    if (lane < G) {
+      const int64_t lp = (static_cast<int64_t>(t.unit) << p.group_shift) + lane;
+      if (ts.mode == kSingle && task == static_cast<int32_t>(blockIdx.x)) {
+        phys = ts.first_phys_raw;
+      } else if (lp < p.block_table_width) {
+        phys = p.block_table[static_cast<int64_t>(t.req) * p.block_table_ld + lp];
+      }
+      if (phys >= p.num_blocks) phys = -1;
+    }
+    if (phys < 0) phys = -1;
+    if (__ballot(phys >= 0) == 0) continue;  // every page of the group skipped
+    move_group<SH, M, LAYOUT>(p, static_cast<int32_t>(phys), static_cast<uint32_t>(t.gbeg),
+                              static_cast<uint32_t>(rows) * cpr, p.dst + t.out_begin * p.dst_row_stride, scale);
   }
 }
 
@@ -856,7 +1070,8 @@ __global__ __launch_bounds__(256) void expand_tasks_kernel(GatherParams p, const
     t.page_begin = g.pbeg;
     t.page_end = g.pend;
     t.out_begin = static_cast<int32_t>(g.out_begin);
-    t.phys = static_cast<int32_t>(lookup_block(p, r, g.logical));
+    // group tasks look their pages up in the gather kernel
+    t.phys = p.group_shift > 0 ? -1 : static_cast<int32_t>(lookup_block(p, r, g.logical));
     t.pad0 = 0;
     t.pad1 = 0;
     out[task] = t;

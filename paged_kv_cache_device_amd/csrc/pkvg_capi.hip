@@ -113,13 +113,21 @@ int32_t task_mode(const GatherParams& p) {
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_shape(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
   return launch(pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC>, grid, SH::threads, lds, stream,
-                p.cu_seq_lens, p.block_table, p.seq_starts, task_mode(p), p.num_reqs, p.block_size,
-                p.block_size_magic, p.block_table_width, p.cu_terminal, p.num_tokens, p);
+                p.cu_seq_lens, p.block_table, p.seq_starts, task_mode(p) | (p.split_shift << 8), p.num_reqs,
+                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens, p);
+}
+
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+hipError_t launch_groups(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
+  return launch(pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC>, grid, SH::threads, lds, stream,
+                p.cu_seq_lens, p.block_table, p.seq_starts, task_mode(p) | (p.group_shift << 8), p.num_reqs,
+                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens, p);
 }
 
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  const int64_t page_out = int64_t(p.block_size) * p.row_in_bytes * (CONVERT == pkvg::kFp8Bf16 ? 2 : 1);
+  if (p.group_shift > 0) return launch_groups<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  const int64_t page_out = int64_t(p.task_tokens) * p.row_in_bytes * (CONVERT == pkvg::kFp8Bf16 ? 2 : 1);
   if (page_out <= kSmallMaxPageBytes)
     return launch_shape<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
   if (page_out <= kMidMaxPageBytes) return launch_shape<pkvg::Mid, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
@@ -218,10 +226,65 @@ void fill_common(Plan& pl, const void* src, void* dst, const int32_t* block_tabl
   pl.p.block_table_width = block_table_width;
   pl.p.num_reqs = num_reqs;
   pl.p.num_blocks = num_blocks;
-  pl.p.block_size = block_size;
-  pl.p.block_size_magic = magic_for(static_cast<uint32_t>(block_size));
+  pl.p.task_tokens = block_size;
+  pl.p.task_tokens_magic = magic_for(static_cast<uint32_t>(block_size));
+  pl.p.split_shift = 0;
+  pl.p.group_shift = 0;
   pl.p.num_tokens = num_tokens;
   pl.capacity = num_tokens / block_size + 2 * int64_t(num_reqs) + 1;
+}
+
+// Pages of more than one narrow batch of output (256 lanes x 288 bytes) are
+// split into 2^k equal task units, halving while the unit is an even number of
+// tokens and still larger than that batch: a few large pages then spread over
+// the whole chip instead of leaving most CUs idle (240 pages of 256 tokens
+// would fill 240 of 256 CUs with one workgroup each).  Splitting only when the
+// task count stays within int32.
+constexpr int64_t kSplitAboveBytes = int64_t(pkvg::Narrow::threads) * pkvg::Narrow::lane_bytes;
+
+// Small pages go to the group kernel, whose task is G = 2^k consecutive pages
+// of one request: the largest G <= 64 whose pages fill at most one small-shape
+// batch (20 KiB of output).  Measured on one request of 61,440 (raw) or
+// 307,200 (fp8) tokens with 1152-byte output rows: as groups, 1-token pages
+// are 2.9x (raw) and 4.3x (fp8) faster, 2-token raw pages 1.6x, 4-token raw
+// pages the same; 8-token raw pages are 8% faster one per workgroup, 8-token
+// fp8 pages 7% slower.  Batches of many short requests gain 1.1-5.9x from 8-
+// down to 1-token pages (the page kernel's workgroups each build the task
+// prefix for one small page).  So: pages of at most 4.5 KiB of output always,
+// of at most 9 KiB for batches and fp8.
+constexpr int64_t kGroupMaxPageBytes = 4608;
+constexpr int64_t kGroupMaxPageBytesBatchOrFp8 = 9216;
+constexpr int32_t kMaxGroupShift = 6;
+
+void plan_group(Plan& pl, int64_t row_out_bytes) {
+  const int32_t bs = pl.p.task_tokens;
+  const int64_t page_out = int64_t(bs) * row_out_bytes;
+  const bool batch_or_fp8 = pl.p.num_reqs > 1 || pl.convert == pkvg::kFp8Bf16;
+  if (page_out > (batch_or_fp8 ? kGroupMaxPageBytesBatchOrFp8 : kGroupMaxPageBytes)) return;
+  int32_t k = 0;
+  while (k < kMaxGroupShift && (page_out << (k + 1)) <= kSmallMaxPageBytes) ++k;
+  if (k == 0) return;
+  pl.p.page_tokens = bs;
+  pl.p.page_tokens_magic = magic_for(static_cast<uint32_t>(bs));
+  pl.p.task_tokens = bs << k;
+  pl.p.task_tokens_magic = magic_for(static_cast<uint32_t>(bs << k));
+  pl.p.group_shift = k;
+  pl.capacity = pl.p.num_tokens / (int64_t(bs) << k) + 2 * int64_t(pl.p.num_reqs) + 1;
+}
+
+void plan_split(Plan& pl, int64_t row_out_bytes) {
+  int32_t tt = pl.p.task_tokens;
+  int32_t k = 0;
+  while ((tt & 1) == 0 && int64_t(tt) * row_out_bytes > kSplitAboveBytes) {
+    tt >>= 1;
+    ++k;
+  }
+  const int64_t capacity = pl.p.num_tokens / tt + 2 * int64_t(pl.p.num_reqs) + 1;
+  if (k == 0 || capacity >= (int64_t(1) << 31)) return;
+  pl.p.task_tokens = tt;
+  pl.p.task_tokens_magic = magic_for(static_cast<uint32_t>(tt));
+  pl.p.split_shift = k;
+  pl.capacity = capacity;
 }
 
 // Raw copy plan: pick the widest access that every row, stride and base allows.
@@ -308,6 +371,8 @@ int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, 
   st = plan_copy(pl, src_cache, dst, elem_bytes, entry, src_block_stride, src_token_stride, dst_row_stride,
                  block_size);
   if (st != PKVG_OK) return st;
+  plan_split(pl, int64_t(entry) * elem_bytes);
+  plan_group(pl, int64_t(entry) * elem_bytes);
   return run_plan(pl, static_cast<hipStream_t>(stream));
 }
 
@@ -329,6 +394,8 @@ static int gather_fp8_common(const void* src_cache, int64_t num_blocks, int32_t 
   pl.p.scale = scale;
   st = plan_fp8(pl, src_cache, dst, entry, src_block_stride, src_token_stride, dst_row_stride, block_size);
   if (st != PKVG_OK) return st;
+  plan_split(pl, 2 * int64_t(entry));
+  plan_group(pl, 2 * int64_t(entry));
   return run_plan(pl, static_cast<hipStream_t>(stream));
 }
 
@@ -381,8 +448,9 @@ int gather_page_tasks(const int32_t* cu_seq_lens, int32_t cu_terminal, const int
   p.block_table_width = block_table_width;
   p.num_reqs = num_reqs;
   p.num_blocks = num_blocks;
-  p.block_size = block_size;
-  p.block_size_magic = magic_for(static_cast<uint32_t>(block_size));
+  p.task_tokens = block_size;  // one task per page
+  p.task_tokens_magic = magic_for(static_cast<uint32_t>(block_size));
+  p.split_shift = 0;
   p.num_tokens = num_tokens;
   void* scratch = nullptr;
   hipError_t e = hipMallocAsync(&scratch, sizeof(int32_t) * (size_t(num_reqs) + 1), s);

@@ -170,6 +170,67 @@ def test_large_pages(bs, lens, kind):
     check_parity(wl, DEV)
 
 
+def _with_holes(wl, seed):
+    """A copy of `wl` with guard-skipped pages: a few table entries set to -1 or
+    past the cache, and the table cut a few columns short."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    bt = wl.block_table.clone()
+    flat = bt.view(-1)
+    if flat.numel() > 0:
+        for k in range(min(7, flat.numel())):
+            flat[int(torch.randint(0, flat.numel(), (1,), generator=g))] = [-1, wl.num_blocks, 1 << 30][k % 3]
+    wl.block_table = bt[:, : max(bt.shape[1] - 3, 0)].contiguous()
+    return wl
+
+
+@pytest.mark.parametrize("bs,R,kind,pad", [
+    (1, 1, workloads.RAW, False),
+    (1, 1, workloads.UPCONVERT, False),
+    (1, 300, workloads.DEQUANT_FP8, True),
+    (2, 5, workloads.RAW, True),
+    (3, 1, workloads.DEQUANT_FP8, True),
+    (4, 70, workloads.RAW, False),
+    (5, 1200, workloads.RAW, False),
+    (8, 1, workloads.UPCONVERT, False),
+    (7, 40, workloads.UPCONVERT, True),
+])
+def test_small_page_groups(bs, R, kind, pad):
+    """Pages of one to eight tokens, moved as groups of consecutive pages per
+    workgroup: requests that start and end inside a group, every task path,
+    padded rows (strided copies, unaligned fp8 code rows), then guard-skipped
+    pages inside groups and a table that ends mid-request."""
+    g = torch.Generator("cpu").manual_seed(bs * 1000 + R)
+    hi = max(40_000 // R, 3)
+    lens = [int(x) for x in torch.randint(0, hi, (R,), generator=g)]
+    starts = [int(torch.randint(0, n // 2 + 1, (1,), generator=g)) for n in lens]
+    pages = sum(-(-n // bs) for n in lens)
+    wl = workloads.make_workload(f"groups_{bs}_{R}_{kind}", kind, lens, bs, 576, pages + 11, seed=bs + R,
+                                 starts=starts, scale=0.05, cache_cols=577 if pad else 576,
+                                 dst_cols=580 if pad else 576)
+    check_parity(wl, DEV)
+    check_parity(_with_holes(wl, bs + R), DEV)
+
+
+@pytest.mark.parametrize("bs,lens,kind", [
+    (128, [61440], workloads.RAW),
+    (256, [30000, 5, 0, 777], workloads.UPCONVERT),
+    (512, [100000], workloads.DEQUANT_FP8),
+    (256, [2000] * 100, workloads.RAW),
+    (128, [300] * 1100, workloads.RAW),
+    (96, [20000, 3], workloads.UPCONVERT),
+])
+def test_split_pages(bs, lens, kind):
+    """Pages of more than 64 rows of 1152 output bytes, split into 2^k task
+    units of one page each: seq_starts inside a unit, every task path, then
+    guard-skipped pages (all units of a skipped page stay untouched)."""
+    starts = [n // 5 for n in lens]
+    pages = sum(-(-n // bs) for n in lens)
+    wl = workloads.make_workload(f"split_{bs}_{len(lens)}_{kind}", kind, lens, bs, 576, pages + 3,
+                                 seed=bs + len(lens), starts=starts, scale=0.05)
+    check_parity(wl, DEV)
+    check_parity(_with_holes(wl, bs), DEV)
+
+
 def medium_random_workload(seed: int) -> workloads.Workload:
     """A seeded mid-size batch: every workgroup shape (page sizes from a few KiB
     to over 72 KiB), every task path (one request, wave registers, LDS prefix,

@@ -59,6 +59,14 @@ def test_named_workload_sizes():
     assert wl.num_reqs == 64 and wl.cache_base.shape[2] == 577 and wl.workspace.shape[1] == 580
     assert wl.src_cache().stride() == (64 * 577, 577, 1) and wl.dst().stride() == (580, 1)
     assert all(0 <= n <= 65536 for n in wl.context_lens)
+    # page-size variants: 61,440 one-token pages, 60 pages of 1,024 tokens,
+    # 512 requests of 200 one-token pages
+    for name, tokens, bs, width in (("single_60k_bs1_raw", 61440, 1, 61440),
+                                    ("single_60k_bs1024_raw", 61440, 1024, 60),
+                                    ("batch512x200_bs1_raw", 512 * 200, 1, 200)):
+        wl = workloads.named(name)
+        assert (wl.num_tokens, wl.block_size, wl.block_table.shape[1]) == (tokens, bs, width), name
+        assert wl.algorithmic_bytes() == 2304 * tokens + 4 * (wl.num_reqs + 1), name
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -315,6 +315,23 @@ def batch_raw(R: int, bs: int, seed: int, kind: str = RAW) -> Workload:
     return make_workload(name, kind, [n] * R, bs, 576, R * (-(-n // bs)) + 8, seed=seed, scale=0.0625)
 
 
+def page_size_single(bs: int, tokens: int, seed: int, kind: str = RAW) -> Workload:
+    """One request of `tokens` tokens at block size `bs` (entry 576, shuffled
+    blocks): the headline single-request gathers with very small or very large
+    pages.  Not a scenario of the pages: block size is a runtime argument, and
+    these check that one-token pages (moved in groups) and pages of a thousand
+    tokens (split into parts) keep the headline rate."""
+    tag = "fp8_upconvert" if kind in FP8_KINDS else "raw"
+    name = f"single_{tokens // 1024}k_bs{bs}_{tag}"
+    return make_workload(name, kind, [tokens], bs, 576, -(-tokens // bs) * 5 // 4 + 8, seed=seed, scale=0.0625)
+
+
+def short_batch(R: int, n: int, bs: int, seed: int) -> Workload:
+    """R raw requests of n tokens each at block size bs (entry 576, shuffled
+    blocks): many short requests on one-token pages."""
+    return make_workload(f"batch{R}x{n}_bs{bs}_raw", RAW, [n] * R, bs, 576, R * (-(-n // bs)) + 8, seed=seed)
+
+
 NAMED = {
     "tiny_raw": tiny_raw,
     "single_60k_raw": single_60k_raw,
@@ -328,6 +345,10 @@ NAMED = {
     "batch512_bs32_raw": lambda: batch_raw(512, 32, 1103),
     "batch512_bs64_raw": lambda: batch_raw(512, 64, 1104),
     "batch512_bs64_fp8": lambda: batch_raw(512, 64, 1105, UPCONVERT),
+    "single_60k_bs1_raw": lambda: page_size_single(1, 61440, 1201),
+    "single_300k_bs1_fp8_upconvert": lambda: page_size_single(1, 307200, 1202, UPCONVERT),
+    "single_60k_bs1024_raw": lambda: page_size_single(1024, 61440, 1203),
+    "batch512x200_bs1_raw": lambda: short_batch(512, 200, 1, 1204),
 }
 
 
