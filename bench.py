@@ -91,7 +91,8 @@ def summarize_counters(prof_dir: str, workload: str, calib_mib: int, command: st
     out = {}
     for kind, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
         rs = [r for r in rows(kind) if r["Counter_Name"] == counter]
-        gather = [float(r["Counter_Value"]) for r in rs if "gather_pages_kernel" in r["Kernel_Name"]]
+        gather = [float(r["Counter_Value"]) for r in rs
+                  if "gather_pages_kernel" in r["Kernel_Name"] or "gather_groups_kernel" in r["Kernel_Name"]]
         copies = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]][-10:]
         known = calib_mib << 20
         factor = known / (statistics.median(copies) * 1024.0)
