@@ -242,6 +242,15 @@ void fill_common(Plan& pl, const void* src, void* dst, const int32_t* block_tabl
 // task count stays within int32.
 constexpr int64_t kSplitAboveBytes = int64_t(pkvg::Narrow::threads) * pkvg::Narrow::lane_bytes;
 
+// One request's raw pages are split further, into units of at most 9 KiB
+// (8 tokens of 1152-byte rows), which take the small shape.  Measured: the
+// 61,440-token gather on 64-token pages 26.6 -> 25.4 us, the 307,200-token
+// one 120.4 -> 118.9 us, 1,024-token pages 26.0 -> 25.3 us; 18 KiB and 36 KiB
+// units gain less or lose.  Batches lose (every workgroup builds the task
+// prefix: skew-8 +4%, 512 requests +15%) and fp8 pages lose (the 307,200-token
+// upconvert +14%), so both keep the 72 KiB units.
+constexpr int64_t kSplitSingleRawBytes = 9 * 1024;
+
 // Small pages go to the group kernel, whose task is G = 2^k consecutive pages
 // of one request: the largest G <= 64 whose pages fill at most one small-shape
 // batch (20 KiB of output).  Measured on one request of 61,440 (raw) or
@@ -257,6 +266,7 @@ constexpr int64_t kGroupMaxPageBytesBatchOrFp8 = 9216;
 constexpr int32_t kMaxGroupShift = 6;
 
 void plan_group(Plan& pl, int64_t row_out_bytes) {
+  if (pl.p.split_shift > 0) return;  // units are already parts of a page
   const int32_t bs = pl.p.task_tokens;
   const int64_t page_out = int64_t(bs) * row_out_bytes;
   const bool batch_or_fp8 = pl.p.num_reqs > 1 || pl.convert == pkvg::kFp8Bf16;
@@ -272,10 +282,10 @@ void plan_group(Plan& pl, int64_t row_out_bytes) {
   pl.capacity = pl.p.num_tokens / (int64_t(bs) << k) + 2 * int64_t(pl.p.num_reqs) + 1;
 }
 
-void plan_split(Plan& pl, int64_t row_out_bytes) {
+void plan_split(Plan& pl, int64_t row_out_bytes, int64_t max_unit_bytes) {
   int32_t tt = pl.p.task_tokens;
   int32_t k = 0;
-  while ((tt & 1) == 0 && int64_t(tt) * row_out_bytes > kSplitAboveBytes) {
+  while ((tt & 1) == 0 && int64_t(tt) * row_out_bytes > max_unit_bytes) {
     tt >>= 1;
     ++k;
   }
@@ -371,7 +381,7 @@ int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, 
   st = plan_copy(pl, src_cache, dst, elem_bytes, entry, src_block_stride, src_token_stride, dst_row_stride,
                  block_size);
   if (st != PKVG_OK) return st;
-  plan_split(pl, int64_t(entry) * elem_bytes);
+  plan_split(pl, int64_t(entry) * elem_bytes, num_reqs == 1 ? kSplitSingleRawBytes : kSplitAboveBytes);
   plan_group(pl, int64_t(entry) * elem_bytes);
   return run_plan(pl, static_cast<hipStream_t>(stream));
 }
@@ -394,7 +404,7 @@ static int gather_fp8_common(const void* src_cache, int64_t num_blocks, int32_t 
   pl.p.scale = scale;
   st = plan_fp8(pl, src_cache, dst, entry, src_block_stride, src_token_stride, dst_row_stride, block_size);
   if (st != PKVG_OK) return st;
-  plan_split(pl, 2 * int64_t(entry));
+  plan_split(pl, 2 * int64_t(entry), kSplitAboveBytes);
   plan_group(pl, 2 * int64_t(entry));
   return run_plan(pl, static_cast<hipStream_t>(stream));
 }
