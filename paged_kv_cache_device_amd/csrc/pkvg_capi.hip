@@ -252,15 +252,19 @@ constexpr int64_t kSplitAboveBytes = int64_t(pkvg::Narrow::threads) * pkvg::Narr
 constexpr int64_t kSplitSingleRawBytes = 9 * 1024;
 
 // Small pages go to the group kernel, whose task is G = 2^k consecutive pages
-// of one request: the largest G <= 64 whose pages fill at most one small-shape
-// batch (20 KiB of output).  Measured on one request of 61,440 (raw) or
-// 307,200 (fp8) tokens with 1152-byte output rows: as groups, 1-token pages
-// are 2.9x (raw) and 4.3x (fp8) faster, 2-token raw pages 1.6x, 4-token raw
-// pages the same; 8-token raw pages are 8% faster one per workgroup, 8-token
-// fp8 pages 7% slower.  Batches of many short requests gain 1.1-5.9x from 8-
-// down to 1-token pages (the page kernel's workgroups each build the task
-// prefix for one small page).  So: pages of at most 4.5 KiB of output always,
-// of at most 9 KiB for batches and fp8.
+// of one request (always the small shape).  Which pages, measured on one
+// request of 61,440 (raw) or 307,200 (fp8) tokens with 1152-byte output rows:
+// as groups, 1-token pages are 2.9x (raw) and 4.3x (fp8) faster, 2-token raw
+// pages 1.6x, 4-token raw pages the same; 8-token raw pages are 8% faster one
+// per workgroup, 8-token fp8 pages 7% slower.  Batches of many short requests
+// gain 1.1-5.9x from 8- down to 1-token pages (the page kernel's workgroups
+// each build the task prefix for one small page).  So: pages of at most
+// 4.5 KiB of output always, of at most 9 KiB for batches and fp8.
+// How many: the largest G <= 64 whose pages hold at most 9 KiB of output (one
+// request, raw), 20 KiB (one request, fp8) or 36 KiB (batches).  Against 20 KiB
+// groups, one request's raw 1- and 2-token pages take 1.8% less time in 9 KiB
+// groups (its fp8 pages 4% more), and 512-request batches 1.5% less in 36 KiB
+// groups (single requests 5% more).
 constexpr int64_t kGroupMaxPageBytes = 4608;
 constexpr int64_t kGroupMaxPageBytesBatchOrFp8 = 9216;
 constexpr int32_t kMaxGroupShift = 6;
@@ -271,8 +275,10 @@ void plan_group(Plan& pl, int64_t row_out_bytes) {
   const int64_t page_out = int64_t(bs) * row_out_bytes;
   const bool batch_or_fp8 = pl.p.num_reqs > 1 || pl.convert == pkvg::kFp8Bf16;
   if (page_out > (batch_or_fp8 ? kGroupMaxPageBytesBatchOrFp8 : kGroupMaxPageBytes)) return;
+  const int64_t max_group_bytes =
+      pl.p.num_reqs > 1 ? kMidMaxPageBytes : (pl.convert == pkvg::kFp8Bf16 ? kSmallMaxPageBytes : kSplitSingleRawBytes);
   int32_t k = 0;
-  while (k < kMaxGroupShift && (page_out << (k + 1)) <= kSmallMaxPageBytes) ++k;
+  while (k < kMaxGroupShift && (page_out << (k + 1)) <= max_group_bytes) ++k;
   if (k == 0) return;
   pl.p.page_tokens = bs;
   pl.p.page_tokens_magic = magic_for(static_cast<uint32_t>(bs));

@@ -468,6 +468,19 @@ def test_single_request(tokens, start, bs, kind):
     check_parity(wl, DEV)
 
 
+@pytest.mark.parametrize("bs", [64, 128, 24, 40, 1000])
+def test_single_request_units(bs):
+    """One request's raw pages move as units of at most 9 KiB (1152-byte rows:
+    8 tokens of a 64-token page, 6 of a 24-token page, 5 of a 40-token page,
+    125 of a 1,000-token page after three halvings): seq_starts on and beside
+    unit and page boundaries, a table narrower than the request, holes."""
+    for start in (1, 4, 5, 6, 7, 8, 9, bs - 1, bs, bs + 1, 3 * bs + 5):
+        wl = workloads.make_workload(f"units_{bs}_{start}", workloads.RAW, [start + 3000 + bs // 3], bs, 576,
+                                     -(-(start + 3000 + bs) // bs) + 4, seed=bs * 100 + start, starts=[start])
+        check_parity(wl, DEV)
+    check_parity(_with_holes(wl, bs), DEV)
+
+
 @pytest.mark.parametrize("kind", [workloads.RAW, workloads.UPCONVERT])
 def test_single_request_prologue_edges(kind):
     """The single-request prologue reads its three metadata values without a
