@@ -251,6 +251,14 @@ constexpr int64_t kSplitAboveBytes = int64_t(pkvg::Narrow::threads) * pkvg::Narr
 // upconvert +14%), so both keep the 72 KiB units.
 constexpr int64_t kSplitSingleRawBytes = 9 * 1024;
 
+// Raw pages of batches of more than 64 requests (the LDS-prefix and task-table
+// paths) are split into units of at most 36 KiB (mid shape).  Measured on
+// 64-token pages: 65 x 2000 tokens -6%, 128 x 800 -1.6%, 300 x 3000 -5.5%,
+// 512 x 200 -5%, 1024 x 200 -1.6%, 2048 x 100 -6%; 18 KiB units gain less or
+// lose.  Batches of at most 64 requests (wave-register prefix) lose (skew-8
+// +5%) and fp8 batches gain nothing; both keep 72 KiB units.
+constexpr int64_t kSplitBatchRawBytes = 36 * 1024;
+
 // Small pages go to the group kernel, whose task is G = 2^k consecutive pages
 // of one request (always the small shape).  Which pages, measured on one
 // request of 61,440 (raw) or 307,200 (fp8) tokens with 1152-byte output rows:
@@ -387,7 +395,9 @@ int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, 
   st = plan_copy(pl, src_cache, dst, elem_bytes, entry, src_block_stride, src_token_stride, dst_row_stride,
                  block_size);
   if (st != PKVG_OK) return st;
-  plan_split(pl, int64_t(entry) * elem_bytes, num_reqs == 1 ? kSplitSingleRawBytes : kSplitAboveBytes);
+  plan_split(pl, int64_t(entry) * elem_bytes,
+             num_reqs == 1 ? kSplitSingleRawBytes
+                           : (num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchRawBytes : kSplitAboveBytes));
   plan_group(pl, int64_t(entry) * elem_bytes);
   return run_plan(pl, static_cast<hipStream_t>(stream));
 }
