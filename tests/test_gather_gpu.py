@@ -519,20 +519,22 @@ def test_empty_block_table(R):
 # capture in a HIP graph: every replay recomputes from the current inputs
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("entry", [64, 576])
 @pytest.mark.parametrize("kind,R", [(workloads.RAW, 1), (workloads.UPCONVERT, 5),
                                     (workloads.DEQUANT_FP8, 100), (workloads.RAW, 1500)])
-def test_graph_replays(kind, R):
+def test_graph_replays(kind, R, entry):
     """The calls enqueue only kernel launches (up to 1024 requests) or kernel
     launches between a stream-ordered allocation and its free (more requests),
     and no memset, so they can be captured.  Between replays the cache
     contents change and eager work runs; each replay must match the oracle on
-    the inputs of that moment."""
+    the inputs of that moment.  16-token pages of 64-element rows go to the
+    group kernel, of 576-element rows to the page kernel."""
     import paged_kv_cache_device_amd as pkvg
 
     g = torch.Generator("cpu").manual_seed(R)
     lens = torch.randint(1, 300, (R,), generator=g).tolist()
     starts = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in lens]
-    wl = workloads.make_workload(f"graph_{kind}_{R}", kind, lens, 16, 64,
+    wl = workloads.make_workload(f"graph_{kind}_{R}_{entry}", kind, lens, 16, entry,
                                  sum(-(-n // 16) for n in lens) + 2, seed=R, starts=starts,
                                  scale=0.05, workspace_rows=sum(lens) + 4)
     d = wl.to(DEV)
@@ -556,7 +558,7 @@ def test_graph_replays(kind, R):
     for rep in range(4):
         log(f"[graph] {kind} R={R} replay {rep}")
         # new cache contents in place (the graph holds the same pointers)
-        fresh = workloads.make_workload("tmp", kind, lens, 16, 64, wl.num_blocks, seed=100 + rep,
+        fresh = workloads.make_workload("tmp", kind, lens, 16, entry, wl.num_blocks, seed=100 + rep,
                                         starts=starts, scale=0.05)
         wl.cache_base.copy_(fresh.cache_base)
         d.cache_base.copy_(fresh.cache_base)
@@ -573,19 +575,21 @@ def test_graph_replays(kind, R):
 # the open-ended cu_seq_lens convention (no terminal entry)
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("entry", [64, 576])
 @pytest.mark.parametrize("R,kind", [(1, workloads.RAW), (7, workloads.UPCONVERT),
                                     (200, workloads.DEQUANT_FP8), (1500, workloads.RAW)])
-def test_open_ended_cu_seq_lens(R, kind):
+def test_open_ended_cu_seq_lens(R, kind, entry):
     """cu_seq_lens holds only the R starts; the last request runs to num_tokens.
     On the device the array is followed by a poisoned entry, so a kernel that
     read a terminal entry would write the wrong rows.  Covers the single-request,
-    wave-register, LDS-prefix and task-table paths."""
+    wave-register, LDS-prefix and task-table paths, in the group kernel (64-
+    element rows) and the page kernel (576-element rows)."""
     import paged_kv_cache_device_amd as pkvg
 
     g = torch.Generator("cpu").manual_seed(R + 7)
     lens = torch.randint(1, 200, (R,), generator=g).tolist()
     starts = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in lens]
-    wl = workloads.make_workload(f"open_{R}_{kind}", kind, lens, 16, 64,
+    wl = workloads.make_workload(f"open_{R}_{kind}_{entry}", kind, lens, 16, entry,
                                  sum(-(-n // 16) for n in lens) + 2, seed=R, starts=starts,
                                  scale=0.05, workspace_rows=sum(lens) + 8).open_ended()
     want, _ = oracle.run_workload(wl)
