@@ -199,6 +199,62 @@ int gather_page_tasks(const int32_t *cu_seq_lens, int32_t cu_terminal, const int
                       int32_t *tasks, int64_t capacity, int32_t *num_tasks,
                       void *stream);
 
+/*
+ * pkvg_plan -- how a gather call with these arguments would run, worked out
+ * by the same host code as the call itself, without enqueueing anything or
+ * touching a device: pointers are checked for NULL and alignment only and are
+ * never read.  For tests of the host's choices, and for tuning.
+ *
+ *   op     PKVG_OP_GATHER_CACHE, PKVG_OP_GATHER_MAYBE_DEQUANT or
+ *          PKVG_OP_GATHER_UPCONVERT_FP8
+ *   kind   the call's elem_bytes (gather_cache) or kv_cache_dtype
+ *          (gather_maybe_dequant); ignored for the upconvert
+ *   scale  as for the fp8 calls (checked for NULL only)
+ *   the other arguments as for the call (no stream)
+ *   info   host pointer, filled on PKVG_OK (all zero when the call has no work)
+ *
+ * Returns what the call would return from its argument checks (never
+ * PKVG_E_HIP), PKVG_E_SHAPE for an unknown op, PKVG_E_NULL for a NULL info.
+ */
+#define PKVG_OP_GATHER_CACHE 0
+#define PKVG_OP_GATHER_MAYBE_DEQUANT 1
+#define PKVG_OP_GATHER_UPCONVERT_FP8 2
+
+#define PKVG_KERNEL_PAGES 0   /* one task = one logical page, or one of 2^split_shift equal parts of it */
+#define PKVG_KERNEL_GROUPS 1  /* one task = 2^group_shift consecutive logical pages of one request */
+
+#define PKVG_TASKS_WAVE 0     /* task prefix built in wave registers (2..64 requests) */
+#define PKVG_TASKS_LDS 1      /* task prefix built in LDS (65..PKVG_FUSED_MAX_REQS requests) */
+#define PKVG_TASKS_TABLE 2    /* task table built by two kernels first (more requests) */
+#define PKVG_TASKS_SINGLE 3   /* one request: no prefix */
+
+typedef struct pkvg_plan_info {
+  int32_t kernel;        /* PKVG_KERNEL_* */
+  int32_t threads;       /* workgroup size */
+  int32_t batch_bytes;   /* output bytes one workgroup moves per batch of loads */
+  int32_t task_mode;     /* PKVG_TASKS_* */
+  int32_t convert;       /* 0: bit copy; 1: fp8 e4m3fn -> bf16 */
+  int32_t access_width;  /* bytes (copy) or codes (fp8) per lane access */
+  int32_t flat;          /* 1: source token stride and destination row stride equal the row bytes */
+  int32_t src_vector;    /* fp8: 1 when code rows are read as aligned words */
+  int32_t task_tokens;   /* tokens per task unit */
+  int32_t split_shift;   /* a page is 2^split_shift task units */
+  int32_t group_shift;   /* a task unit is 2^group_shift pages */
+  int32_t reserved;      /* 0 */
+  int64_t grid;          /* workgroups launched */
+  int64_t task_capacity; /* upper bound on the number of task units */
+} pkvg_plan_info;
+
+int pkvg_plan(int32_t op, int32_t kind, const void *src_cache,
+              int64_t num_blocks, int32_t block_size, int32_t entry,
+              int64_t src_block_stride, int64_t src_token_stride,
+              void *dst, int64_t num_tokens, int64_t dst_row_stride,
+              const int32_t *block_table, int32_t block_table_width,
+              int64_t block_table_ld,
+              const int32_t *cu_seq_lens, int32_t cu_terminal,
+              const int32_t *seq_starts,
+              int32_t num_reqs, const float *scale, pkvg_plan_info *info);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *pkvg_status_string(int status);
 

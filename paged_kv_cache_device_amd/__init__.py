@@ -16,6 +16,8 @@ Entry points (names as in the C ABI):
   seq_starts=None)``
 * ``gather_page_tasks(cu_seq_lens, seq_starts, batch_size, num_tokens, block_size,
   block_table, num_blocks, capacity=None)``
+* ``pkvg_plan(op, kind, ...)``: how a call would run (kernel, shape, task units,
+  grid), from plain sizes, strides and addresses; nothing is enqueued
 
 ``src_cache`` is a [num_blocks, block_size, entry] view (innermost stride 1;
 a view of wider rows is fine), ``dst`` a [num_tokens, entry] view (innermost
@@ -45,6 +47,15 @@ PKVG_E_HIP = 6
 PKVG_KV_AUTO = 0
 PKVG_KV_FP8_E4M3 = 1
 PKVG_TASK_INTS = 8
+PKVG_OP_GATHER_CACHE = 0
+PKVG_OP_GATHER_MAYBE_DEQUANT = 1
+PKVG_OP_GATHER_UPCONVERT_FP8 = 2
+PKVG_KERNEL_PAGES = 0
+PKVG_KERNEL_GROUPS = 1
+PKVG_TASKS_WAVE = 0
+PKVG_TASKS_LDS = 1
+PKVG_TASKS_TABLE = 2
+PKVG_TASKS_SINGLE = 3
 
 # the C entry points and their argument types, as declared in include/pkvg.h
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -55,9 +66,21 @@ SIGNATURES = {
     "gather_upconvert_fp8": [_vp] + _CACHE_ARGS + [_vp, _vp],
     "gather_page_tasks": [_vp, _i32, _vp, _i32, _i64, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp,
                           _vp],
+    "pkvg_plan": [_i32, _i32, _vp] + _CACHE_ARGS + [_vp, _vp],
     "pkvg_status_string": [ctypes.c_int],
     "pkvg_last_hip_error": [],
 }
+
+
+class PlanInfo(ctypes.Structure):
+    """pkvg_plan_info of include/pkvg.h."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kernel", "threads", "batch_bytes", "task_mode", "convert", "access_width", "flat",
+        "src_vector", "task_tokens", "split_shift", "group_shift", "reserved")] + [
+        ("grid", ctypes.c_int64), ("task_capacity", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
 
 
 class PkvgError(RuntimeError):
@@ -314,3 +337,20 @@ def gather_page_tasks(cu_seq_lens: torch.Tensor, seq_starts: torch.Tensor | None
         _ptr(block_table), block_table.shape[1], block_table.stride(0), num_blocks,
         _ptr(tasks), capacity, _ptr(count), _stream_handle()), "gather_page_tasks")
     return tasks[:capacity], count
+
+
+def pkvg_plan(op: int, kind: int, src: int, num_blocks: int, block_size: int, entry: int,
+              src_block_stride: int, src_token_stride: int, dst: int, num_tokens: int,
+              dst_row_stride: int, block_table: int | None, block_table_width: int,
+              block_table_ld: int, cu_seq_lens: int, cu_terminal: int, seq_starts: int | None,
+              num_reqs: int, scale: int | None) -> dict:
+    """How a gather call with these arguments would run (``pkvg_plan`` of the C
+    ABI): addresses are plain integers, checked for NULL and alignment only and
+    never read, so this needs no device.  Raises PkvgError with the status the
+    call itself would return."""
+    info = PlanInfo()
+    _check(library().pkvg_plan(op, kind, src, num_blocks, block_size, entry, src_block_stride,
+                               src_token_stride, dst, num_tokens, dst_row_stride, block_table,
+                               block_table_width, block_table_ld, cu_seq_lens, cu_terminal,
+                               seq_starts, num_reqs, scale, ctypes.byref(info)), "pkvg_plan")
+    return info.as_dict()

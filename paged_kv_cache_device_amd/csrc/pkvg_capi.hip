@@ -16,6 +16,9 @@ using pkvg::GatherParams;
 using pkvg::TaskRecord;
 
 static_assert(pkvg::kFusedMaxReqs == PKVG_FUSED_MAX_REQS, "the fused task paths cover the header's batch limit");
+static_assert(pkvg::kWaveRegs == PKVG_TASKS_WAVE && pkvg::kLdsPrefix == PKVG_TASKS_LDS &&
+                  pkvg::kTable == PKVG_TASKS_TABLE && pkvg::kSingle == PKVG_TASKS_SINGLE,
+              "the header's task-mode codes are the kernel's");
 
 thread_local int g_last_hip_error = 0;
 
@@ -43,7 +46,11 @@ struct Plan {
   int layout = pkvg::kRows;
   bool src_vec = true;
   int64_t capacity = 0;   // upper bound on the number of page tasks
+  int64_t grid = 0;       // workgroups launched
+  int shape = 0;          // workgroup shape (ShapeId)
 };
+
+enum ShapeId : int { kShapeSmall = 0, kShapeMid = 1, kShapeNarrow = 2, kShapeWide = 3 };
 
 // Checks shared by every gather entry point.  Returns PKVG_OK or an error
 // code; `*nothing` is set when there is no work (nothing is launched then).
@@ -124,48 +131,61 @@ hipError_t launch_groups(const GatherParams& p, unsigned grid, size_t lds, hipSt
                 p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens, p);
 }
 
+// The workgroup shape of a plan (the rules above; the group kernel always
+// takes the small shape).
+int shape_for(const Plan& pl) {
+  if (pl.p.group_shift > 0) return kShapeSmall;
+  const int64_t page_out = int64_t(pl.p.task_tokens) * pl.p.row_in_bytes * (pl.convert == pkvg::kFp8Bf16 ? 2 : 1);
+  if (page_out <= kSmallMaxPageBytes) return kShapeSmall;
+  if (page_out <= kMidMaxPageBytes) return kShapeMid;
+  if (pl.p.num_reqs <= pkvg::kWaveMaxReqs &&
+      (pl.grid >= kWideMinTasks || (pl.convert == pkvg::kFp8Bf16 && pl.layout == pkvg::kFlat)))
+    return kShapeWide;
+  return kShapeNarrow;
+}
+
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
-hipError_t launch_gather(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
+hipError_t launch_gather(const Plan& pl, size_t lds, hipStream_t stream) {
+  const GatherParams& p = pl.p;
+  const unsigned grid = static_cast<unsigned>(pl.grid);
   if (p.group_shift > 0) return launch_groups<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
-  const int64_t page_out = int64_t(p.task_tokens) * p.row_in_bytes * (CONVERT == pkvg::kFp8Bf16 ? 2 : 1);
-  if (page_out <= kSmallMaxPageBytes)
-    return launch_shape<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
-  if (page_out <= kMidMaxPageBytes) return launch_shape<pkvg::Mid, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
-  if (p.num_reqs <= pkvg::kWaveMaxReqs &&
-      (grid >= kWideMinTasks || (CONVERT == pkvg::kFp8Bf16 && LAYOUT == pkvg::kFlat)))
-    return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
-  return launch_shape<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  switch (pl.shape) {
+    case kShapeSmall: return launch_shape<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+    case kShapeMid: return launch_shape<pkvg::Mid, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+    case kShapeWide: return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+    default: return launch_shape<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  }
 }
 
 template <int CONVERT, int W, bool SRC_VEC>
-hipError_t launch_layout(const Plan& pl, unsigned grid, size_t lds, hipStream_t stream) {
-  if (pl.layout == pkvg::kFlat) return launch_gather<CONVERT, W, pkvg::kFlat, SRC_VEC>(pl.p, grid, lds, stream);
-  return launch_gather<CONVERT, W, pkvg::kRows, SRC_VEC>(pl.p, grid, lds, stream);
+hipError_t launch_layout(const Plan& pl, size_t lds, hipStream_t stream) {
+  if (pl.layout == pkvg::kFlat) return launch_gather<CONVERT, W, pkvg::kFlat, SRC_VEC>(pl, lds, stream);
+  return launch_gather<CONVERT, W, pkvg::kRows, SRC_VEC>(pl, lds, stream);
 }
 
-hipError_t dispatch(const Plan& pl, unsigned grid, size_t lds, hipStream_t stream) {
+hipError_t dispatch(const Plan& pl, size_t lds, hipStream_t stream) {
   if (pl.convert == pkvg::kCopy) {
     switch (pl.width) {
-      case 16: return launch_layout<pkvg::kCopy, 16, true>(pl, grid, lds, stream);
-      case 8: return launch_layout<pkvg::kCopy, 8, true>(pl, grid, lds, stream);
-      case 4: return launch_layout<pkvg::kCopy, 4, true>(pl, grid, lds, stream);
-      case 2: return launch_layout<pkvg::kCopy, 2, true>(pl, grid, lds, stream);
-      default: return launch_layout<pkvg::kCopy, 1, true>(pl, grid, lds, stream);
+      case 16: return launch_layout<pkvg::kCopy, 16, true>(pl, lds, stream);
+      case 8: return launch_layout<pkvg::kCopy, 8, true>(pl, lds, stream);
+      case 4: return launch_layout<pkvg::kCopy, 4, true>(pl, lds, stream);
+      case 2: return launch_layout<pkvg::kCopy, 2, true>(pl, lds, stream);
+      default: return launch_layout<pkvg::kCopy, 1, true>(pl, lds, stream);
     }
   }
   if (pl.src_vec) {
     switch (pl.width) {
-      case 8: return launch_layout<pkvg::kFp8Bf16, 8, true>(pl, grid, lds, stream);
-      case 4: return launch_layout<pkvg::kFp8Bf16, 4, true>(pl, grid, lds, stream);
-      case 2: return launch_layout<pkvg::kFp8Bf16, 2, true>(pl, grid, lds, stream);
-      default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, grid, lds, stream);
+      case 8: return launch_layout<pkvg::kFp8Bf16, 8, true>(pl, lds, stream);
+      case 4: return launch_layout<pkvg::kFp8Bf16, 4, true>(pl, lds, stream);
+      case 2: return launch_layout<pkvg::kFp8Bf16, 2, true>(pl, lds, stream);
+      default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, lds, stream);
     }
   }
   switch (pl.width) {
-    case 8: return launch_layout<pkvg::kFp8Bf16, 8, false>(pl, grid, lds, stream);
-    case 4: return launch_layout<pkvg::kFp8Bf16, 4, false>(pl, grid, lds, stream);
-    case 2: return launch_layout<pkvg::kFp8Bf16, 2, false>(pl, grid, lds, stream);
-    default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, grid, lds, stream);  // one code: any alignment
+    case 8: return launch_layout<pkvg::kFp8Bf16, 8, false>(pl, lds, stream);
+    case 4: return launch_layout<pkvg::kFp8Bf16, 4, false>(pl, lds, stream);
+    case 2: return launch_layout<pkvg::kFp8Bf16, 2, false>(pl, lds, stream);
+    default: return launch_layout<pkvg::kFp8Bf16, 1, true>(pl, lds, stream);  // one code: any alignment
   }
 }
 
@@ -180,12 +200,17 @@ hipError_t build_tasks(const GatherParams& p, int32_t* P, int32_t* count, TaskRe
                 static_cast<int32_t>(capacity));
 }
 
+// Grid and workgroup shape, once the task units are fixed.
+void finish_plan(Plan& pl) {
+  pl.grid = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
+  pl.shape = shape_for(pl);
+}
+
 int run_plan(Plan& pl, hipStream_t stream) {
   const int32_t R = pl.p.num_reqs;
   if (R <= PKVG_FUSED_MAX_REQS) {
-    const int64_t g = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
     const size_t lds = R <= pkvg::kWaveMaxReqs ? 0 : sizeof(int32_t) * (3 * size_t(R) + 3);
-    hipError_t e = dispatch(pl, static_cast<unsigned>(g), lds, stream);
+    hipError_t e = dispatch(pl, lds, stream);
     return e == hipSuccess ? PKVG_OK : hip_fail(e);
   }
   // large batch: stream-ordered scratch = P[R+1] | count | records[capacity]
@@ -203,8 +228,7 @@ int run_plan(Plan& pl, hipStream_t stream) {
     pl.p.tasks = rec;
     pl.p.task_count = count;
     pl.p.task_capacity = static_cast<int32_t>(pl.capacity);
-    const int64_t g = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
-    e = dispatch(pl, static_cast<unsigned>(g), 0, stream);
+    e = dispatch(pl, 0, stream);
   }
   const hipError_t ef = hipFreeAsync(scratch, stream);
   if (e != hipSuccess) return hip_fail(e);
@@ -374,6 +398,97 @@ int plan_fp8(Plan& pl, const void* src, void* dst, int32_t entry, int64_t sbs, i
   return PKVG_OK;
 }
 
+
+// The arguments every gather call shares (strides in elements, as passed).
+struct GatherArgs {
+  const void* src;
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t entry;
+  int64_t src_block_stride;
+  int64_t src_token_stride;
+  void* dst;
+  int64_t num_tokens;
+  int64_t dst_row_stride;
+  const int32_t* block_table;
+  int32_t block_table_width;
+  int64_t block_table_ld;
+  const int32_t* cu_seq_lens;
+  int32_t cu_terminal;
+  const int32_t* seq_starts;
+  int32_t num_reqs;
+};
+
+// Validates a call and plans it (access width, task units, grid, shape);
+// touches no device.  `kind`: elem_bytes (gather_cache) or kv_cache_dtype
+// (gather_maybe_dequant); unused for the upconvert.  `*nothing` is set when
+// the call has no work.
+int prepare(int32_t op, int32_t kind, const GatherArgs& a, const float* scale, Plan& pl, bool* nothing) {
+  *nothing = false;
+  int32_t elem_bytes = 0;  // raw copy element size; 0: fp8
+  if (op == PKVG_OP_GATHER_CACHE) {
+    if (kind != 1 && kind != 2 && kind != 4 && kind != 8) return PKVG_E_DTYPE;
+    elem_bytes = kind;
+  } else if (op == PKVG_OP_GATHER_MAYBE_DEQUANT) {
+    if (kind == PKVG_KV_AUTO) elem_bytes = 2;
+    else if (kind != PKVG_KV_FP8_E4M3) return PKVG_E_DTYPE;
+  } else if (op != PKVG_OP_GATHER_UPCONVERT_FP8) {
+    return PKVG_E_SHAPE;
+  }
+  int st = check_common(a.src, a.num_blocks, a.block_size, a.entry, a.src_block_stride, a.src_token_stride, a.dst,
+                        a.num_tokens, a.dst_row_stride, a.block_table, a.block_table_width, a.block_table_ld,
+                        a.cu_seq_lens, a.cu_terminal, a.num_reqs, nothing);
+  if (st != PKVG_OK || *nothing) return st;
+  if (elem_bytes == 0 && !scale) return PKVG_E_NULL;
+  fill_common(pl, a.src, a.dst, a.block_table, a.block_table_width, a.block_table_ld, a.cu_seq_lens,
+              a.cu_terminal, a.seq_starts, a.num_reqs, a.num_blocks, a.block_size, a.num_tokens);
+  if (elem_bytes > 0) {
+    st = plan_copy(pl, a.src, a.dst, elem_bytes, a.entry, a.src_block_stride, a.src_token_stride,
+                   a.dst_row_stride, a.block_size);
+    if (st != PKVG_OK) return st;
+    const int64_t row = int64_t(a.entry) * elem_bytes;
+    plan_split(pl, row,
+               a.num_reqs == 1 ? kSplitSingleRawBytes
+                               : (a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchRawBytes : kSplitAboveBytes));
+    plan_group(pl, row);
+  } else {
+    pl.p.scale = scale;
+    st = plan_fp8(pl, a.src, a.dst, a.entry, a.src_block_stride, a.src_token_stride, a.dst_row_stride,
+                  a.block_size);
+    if (st != PKVG_OK) return st;
+    plan_split(pl, 2 * int64_t(a.entry), kSplitAboveBytes);
+    plan_group(pl, 2 * int64_t(a.entry));
+  }
+  finish_plan(pl);
+  return PKVG_OK;
+}
+
+int run_call(int32_t op, int32_t kind, const GatherArgs& a, const float* scale, void* stream) {
+  Plan pl;
+  bool nothing;
+  const int st = prepare(op, kind, a, scale, pl, &nothing);
+  if (st != PKVG_OK || nothing) return st;
+  return run_plan(pl, static_cast<hipStream_t>(stream));
+}
+
+int32_t shape_threads(int shape) {
+  switch (shape) {
+    case kShapeSmall: return pkvg::Small::threads;
+    case kShapeMid: return pkvg::Mid::threads;
+    case kShapeWide: return pkvg::Wide::threads;
+    default: return pkvg::Narrow::threads;
+  }
+}
+
+int32_t shape_lane_bytes(int shape) {
+  switch (shape) {
+    case kShapeSmall: return pkvg::Small::lane_bytes;
+    case kShapeMid: return pkvg::Mid::lane_bytes;
+    case kShapeWide: return pkvg::Wide::lane_bytes;
+    default: return pkvg::Narrow::lane_bytes;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -383,46 +498,10 @@ int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, 
                  int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
                  int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
                  int32_t cu_terminal, const int32_t* seq_starts, int32_t num_reqs, void* stream) {
-  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return PKVG_E_DTYPE;
-  bool nothing;
-  int st = check_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
-                        num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                        cu_seq_lens, cu_terminal, num_reqs, &nothing);
-  if (st != PKVG_OK || nothing) return st;
-  Plan pl;
-  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, cu_terminal,
-              seq_starts, num_reqs, num_blocks, block_size, num_tokens);
-  st = plan_copy(pl, src_cache, dst, elem_bytes, entry, src_block_stride, src_token_stride, dst_row_stride,
-                 block_size);
-  if (st != PKVG_OK) return st;
-  plan_split(pl, int64_t(entry) * elem_bytes,
-             num_reqs == 1 ? kSplitSingleRawBytes
-                           : (num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchRawBytes : kSplitAboveBytes));
-  plan_group(pl, int64_t(entry) * elem_bytes);
-  return run_plan(pl, static_cast<hipStream_t>(stream));
-}
-
-static int gather_fp8_common(const void* src_cache, int64_t num_blocks, int32_t block_size, int32_t entry,
-                             int64_t src_block_stride, int64_t src_token_stride, void* dst,
-                             int64_t num_tokens, int64_t dst_row_stride, const int32_t* block_table,
-                             int32_t block_table_width, int64_t block_table_ld, const int32_t* cu_seq_lens,
-                             int32_t cu_terminal, const int32_t* seq_starts, int32_t num_reqs,
-                             const float* scale, void* stream) {
-  bool nothing;
-  int st = check_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
-                        num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                        cu_seq_lens, cu_terminal, num_reqs, &nothing);
-  if (st != PKVG_OK || nothing) return st;
-  if (!scale) return PKVG_E_NULL;
-  Plan pl;
-  fill_common(pl, src_cache, dst, block_table, block_table_width, block_table_ld, cu_seq_lens, cu_terminal,
-              seq_starts, num_reqs, num_blocks, block_size, num_tokens);
-  pl.p.scale = scale;
-  st = plan_fp8(pl, src_cache, dst, entry, src_block_stride, src_token_stride, dst_row_stride, block_size);
-  if (st != PKVG_OK) return st;
-  plan_split(pl, 2 * int64_t(entry), kSplitAboveBytes);
-  plan_group(pl, 2 * int64_t(entry));
-  return run_plan(pl, static_cast<hipStream_t>(stream));
+  const GatherArgs a{src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                     num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                     cu_seq_lens, cu_terminal, seq_starts, num_reqs};
+  return run_call(PKVG_OP_GATHER_CACHE, elem_bytes, a, nullptr, stream);
 }
 
 int gather_maybe_dequant(const void* src_cache, int32_t kv_cache_dtype, int64_t num_blocks,
@@ -431,14 +510,10 @@ int gather_maybe_dequant(const void* src_cache, int32_t kv_cache_dtype, int64_t 
                          const int32_t* block_table, int32_t block_table_width, int64_t block_table_ld,
                          const int32_t* cu_seq_lens, int32_t cu_terminal, const int32_t* seq_starts,
                          int32_t num_reqs, const float* scale, void* stream) {
-  if (kv_cache_dtype == PKVG_KV_AUTO)
-    return gather_cache(src_cache, 2, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
-                        num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                        cu_seq_lens, cu_terminal, seq_starts, num_reqs, stream);
-  if (kv_cache_dtype != PKVG_KV_FP8_E4M3) return PKVG_E_DTYPE;
-  return gather_fp8_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
-                           num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                           cu_seq_lens, cu_terminal, seq_starts, num_reqs, scale, stream);
+  const GatherArgs a{src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                     num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                     cu_seq_lens, cu_terminal, seq_starts, num_reqs};
+  return run_call(PKVG_OP_GATHER_MAYBE_DEQUANT, kv_cache_dtype, a, scale, stream);
 }
 
 int gather_upconvert_fp8(const void* src_cache, int64_t num_blocks, int32_t block_size, int32_t entry,
@@ -446,9 +521,40 @@ int gather_upconvert_fp8(const void* src_cache, int64_t num_blocks, int32_t bloc
                          int64_t dst_row_stride, const int32_t* block_table, int32_t block_table_width,
                          int64_t block_table_ld, const int32_t* cu_seq_lens, int32_t cu_terminal,
                          const int32_t* seq_starts, int32_t num_reqs, const float* scale, void* stream) {
-  return gather_fp8_common(src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
-                           num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
-                           cu_seq_lens, cu_terminal, seq_starts, num_reqs, scale, stream);
+  const GatherArgs a{src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                     num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                     cu_seq_lens, cu_terminal, seq_starts, num_reqs};
+  return run_call(PKVG_OP_GATHER_UPCONVERT_FP8, 0, a, scale, stream);
+}
+
+int pkvg_plan(int32_t op, int32_t kind, const void* src_cache, int64_t num_blocks, int32_t block_size,
+              int32_t entry, int64_t src_block_stride, int64_t src_token_stride, void* dst, int64_t num_tokens,
+              int64_t dst_row_stride, const int32_t* block_table, int32_t block_table_width,
+              int64_t block_table_ld, const int32_t* cu_seq_lens, int32_t cu_terminal, const int32_t* seq_starts,
+              int32_t num_reqs, const float* scale, pkvg_plan_info* info) {
+  if (!info) return PKVG_E_NULL;
+  *info = pkvg_plan_info{};
+  const GatherArgs a{src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                     num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                     cu_seq_lens, cu_terminal, seq_starts, num_reqs};
+  Plan pl;
+  bool nothing;
+  const int st = prepare(op, kind, a, scale, pl, &nothing);
+  if (st != PKVG_OK || nothing) return st;
+  info->kernel = pl.p.group_shift > 0 ? PKVG_KERNEL_GROUPS : PKVG_KERNEL_PAGES;
+  info->threads = shape_threads(pl.shape);
+  info->batch_bytes = shape_threads(pl.shape) * shape_lane_bytes(pl.shape);
+  info->task_mode = num_reqs > PKVG_FUSED_MAX_REQS ? PKVG_TASKS_TABLE : task_mode(pl.p);
+  info->convert = pl.convert;
+  info->access_width = pl.width;
+  info->flat = pl.layout == pkvg::kFlat ? 1 : 0;
+  info->src_vector = pl.src_vec ? 1 : 0;
+  info->task_tokens = pl.p.task_tokens;
+  info->split_shift = pl.p.split_shift;
+  info->group_shift = pl.p.group_shift;
+  info->grid = pl.grid;
+  info->task_capacity = pl.capacity;
+  return PKVG_OK;
 }
 
 int gather_page_tasks(const int32_t* cu_seq_lens, int32_t cu_terminal, const int32_t* seq_starts,

@@ -1,0 +1,152 @@
+"""The host's launch decisions, on the CPU: pkvg_plan runs the same argument
+checks and planning as the gather calls (access width, task units, kernel,
+workgroup shape, grid) and reports them without touching a device.  Addresses
+below are fake (never read), aligned to 64 KiB unless a case needs otherwise."""
+import ctypes
+import os
+
+import pytest
+
+pkvg = pytest.importorskip("paged_kv_cache_device_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    # another build of the same sources (the sanitizer test's instrumented one)
+    other = os.environ.get("PKVG_TEST_LIBRARY")
+    if other:
+        pkvg._lib = pkvg.library(other)
+        yield
+        pkvg._lib = None
+        return
+    from paged_kv_cache_device_amd import build
+
+    if build.is_stale():
+        build.build()
+    yield
+
+
+F = 0x10000
+RAW, DEQ, UP = pkvg.PKVG_OP_GATHER_CACHE, pkvg.PKVG_OP_GATHER_MAYBE_DEQUANT, pkvg.PKVG_OP_GATHER_UPCONVERT_FP8
+FP8 = pkvg.PKVG_KV_FP8_E4M3
+
+
+def plan(op=RAW, kind=2, bs=64, entry=576, T=61440, R=1, nb=None, ccols=None, dcols=None, starts=False,
+         width=None, src=F, dst=F, scale=F):
+    """A call over a [nb, bs, ccols] cache and a [T, dcols] destination; strides
+    in elements of each tensor (fp8 caches: bytes)."""
+    ccols = entry if ccols is None else ccols
+    dcols = entry if dcols is None else dcols
+    width = -(-T // bs) if width is None else width
+    nb = width * R + 8 if nb is None else nb
+    return pkvg.pkvg_plan(op, kind, src, nb, bs, entry, bs * ccols, ccols, dst, T, dcols, F, width, width, F, 1,
+                          F if starts else None, R, scale)
+
+
+def test_headline_gathers():
+    # one request of 61,440 raw tokens: 64-token pages moved as 8-token units, small shape
+    p = plan()
+    assert (p["kernel"], p["task_mode"], p["threads"], p["batch_bytes"]) == (
+        pkvg.PKVG_KERNEL_PAGES, pkvg.PKVG_TASKS_SINGLE, 256, 20480)
+    assert (p["access_width"], p["flat"], p["task_tokens"], p["split_shift"], p["group_shift"]) == (16, 1, 8, 3, 0)
+    assert p["grid"] == p["task_capacity"] == 61440 // 8 + 3
+    # one request of 307,200 fp8 tokens to bf16: whole 64-token pages, wide shape
+    p = plan(op=UP, kind=0, T=307200)
+    assert (p["threads"], p["batch_bytes"], p["convert"], p["access_width"], p["src_vector"]) == (1024, 81920, 1, 8, 1)
+    assert (p["task_tokens"], p["split_shift"], p["grid"]) == (64, 0, 307200 // 64 + 3)
+    # skew-8: wave-register prefix, 72 KiB pages, wide shape (>= 1024 tasks)
+    p = plan(T=141101, R=8, starts=True, width=2048)
+    assert (p["task_mode"], p["task_tokens"], p["threads"]) == (pkvg.PKVG_TASKS_WAVE, 64, 1024)
+    # the strided fp8 batch: 577-byte code rows (windowed loads), 1160-byte bf16 rows
+    p = plan(op=DEQ, kind=FP8, T=298156, R=64, ccols=577, dcols=580, width=1024)
+    assert (p["flat"], p["src_vector"], p["access_width"], p["task_mode"], p["threads"]) == (
+        0, 0, 8, pkvg.PKVG_TASKS_WAVE, 1024)
+
+
+@pytest.mark.parametrize("op,kind,bs,R,kernel,tokens,split,group,threads", [
+    (RAW, 2, 1, 1, pkvg.PKVG_KERNEL_GROUPS, 8, 0, 3, 256),      # 9 KiB groups of one-token pages
+    (UP, 0, 1, 1, pkvg.PKVG_KERNEL_GROUPS, 16, 0, 4, 256),      # 18 KiB groups (fp8)
+    (RAW, 2, 1, 512, pkvg.PKVG_KERNEL_GROUPS, 32, 0, 5, 256),   # 36 KiB groups (batch)
+    (RAW, 2, 3, 1, pkvg.PKVG_KERNEL_GROUPS, 6, 0, 1, 256),      # 3-token pages in pairs
+    (RAW, 2, 8, 1, pkvg.PKVG_KERNEL_PAGES, 8, 0, 0, 256),       # 9 KiB pages: one per workgroup
+    (UP, 0, 8, 1, pkvg.PKVG_KERNEL_GROUPS, 16, 0, 1, 256),      # ... but grouped for fp8
+    (RAW, 2, 8, 70, pkvg.PKVG_KERNEL_GROUPS, 32, 0, 2, 256),    # ... and for batches
+    (RAW, 2, 16, 1, pkvg.PKVG_KERNEL_PAGES, 8, 1, 0, 256),      # one request: 8-token units
+    (RAW, 2, 96, 1, pkvg.PKVG_KERNEL_PAGES, 6, 4, 0, 256),      # 96 -> 48 -> 24 -> 12 -> 6
+    (RAW, 2, 1024, 1, pkvg.PKVG_KERNEL_PAGES, 8, 7, 0, 256),
+    (UP, 0, 1024, 1, pkvg.PKVG_KERNEL_PAGES, 64, 4, 0, 1024),   # fp8 keeps 72 KiB units
+    (RAW, 2, 1024, 4, pkvg.PKVG_KERNEL_PAGES, 64, 4, 0, 256),   # small batch: 72 KiB units, < 1024: narrow
+    (RAW, 2, 64, 100, pkvg.PKVG_KERNEL_PAGES, 32, 1, 0, 256),   # > 64 requests: 36 KiB units, mid
+    (RAW, 2, 127, 1, pkvg.PKVG_KERNEL_PAGES, 127, 0, 0, 256),   # odd: no split, narrow
+])
+def test_task_units_and_kernels(op, kind, bs, R, kernel, tokens, split, group, threads):
+    p = plan(op=op, kind=kind, bs=bs, R=R, T=61440)
+    assert (p["kernel"], p["task_tokens"], p["split_shift"], p["group_shift"], p["threads"]) == (
+        kernel, tokens, split, group, threads), p
+    # a task unit is a power-of-two part of a page, or a power-of-two group of pages
+    assert p["split_shift"] == 0 or p["group_shift"] == 0
+    assert p["task_tokens"] << p["split_shift"] == bs << p["group_shift"]
+    # one workgroup per task unit (capacity bound: T / unit + 2R + 1)
+    assert p["task_capacity"] == 61440 // p["task_tokens"] + 2 * R + 1 == p["grid"]
+
+
+def test_task_modes():
+    assert plan(R=1)["task_mode"] == pkvg.PKVG_TASKS_SINGLE
+    assert plan(R=2)["task_mode"] == pkvg.PKVG_TASKS_WAVE
+    assert plan(R=64)["task_mode"] == pkvg.PKVG_TASKS_WAVE
+    assert plan(R=65)["task_mode"] == pkvg.PKVG_TASKS_LDS
+    assert plan(R=1024)["task_mode"] == pkvg.PKVG_TASKS_LDS
+    assert plan(R=1025)["task_mode"] == pkvg.PKVG_TASKS_TABLE
+
+
+def test_access_widths():
+    assert plan(entry=575)["access_width"] == 2                       # 1150-byte rows
+    assert plan(entry=578, ccols=578, dcols=580)["access_width"] == 4  # 1156-byte rows, dword strides
+    assert plan(kind=4, entry=6)["access_width"] == 8                  # 24-byte fp32 rows
+    assert plan(kind=1, entry=7)["access_width"] == 1
+    assert plan(dst=F + 2)["access_width"] == 2                        # destination only 2-byte aligned
+    p = plan(op=UP, kind=0, entry=12)                                  # 12 codes per row
+    assert (p["access_width"], p["src_vector"]) == (4, 1)
+    p = plan(op=UP, kind=0, entry=576, ccols=577)                      # odd code-row pitch: windows
+    assert (p["access_width"], p["src_vector"], p["flat"]) == (8, 0, 0)
+
+
+def test_no_work_and_errors():
+    assert plan(T=0) == {k: 0 for k in plan(T=0)}
+    assert plan(R=0)["grid"] == 0
+    with pytest.raises(pkvg.PkvgError) as e:
+        plan(kind=3)
+    assert e.value.status == pkvg.PKVG_E_DTYPE
+    with pytest.raises(pkvg.PkvgError) as e:
+        plan(op=7)
+    assert e.value.status == pkvg.PKVG_E_SHAPE
+    with pytest.raises(pkvg.PkvgError) as e:
+        plan(op=UP, kind=0, scale=None)
+    assert e.value.status == pkvg.PKVG_E_NULL
+    with pytest.raises(pkvg.PkvgError) as e:
+        plan(op=DEQ, kind=9)
+    assert e.value.status == pkvg.PKVG_E_DTYPE
+    with pytest.raises(pkvg.PkvgError) as e:
+        plan(dcols=500)
+    assert e.value.status == pkvg.PKVG_E_STRIDE
+    lib = pkvg.library()
+    assert lib.pkvg_plan(RAW, 2, F, 4, 16, 8, 128, 8, F, 10, 8, F, 2, 2, F, 1, None, 1, None, None) == \
+        pkvg.PKVG_E_NULL
+
+
+@pytest.mark.parametrize("bad", [dict(kind=3), dict(bs=0), dict(entry=0), dict(dcols=100), dict(src=None),
+                                 dict(T=1 << 31)])
+def test_plan_status_matches_the_call(bad):
+    """pkvg_plan returns exactly what gather_cache returns from its checks
+    (both return before any HIP call for these)."""
+    a = dict(kind=2, bs=16, entry=128, T=1000, R=1, src=F, dcols=None)
+    a.update(bad)
+    dcols = a["entry"] if a["dcols"] is None else a["dcols"]
+    width = max(-(-a["T"] // max(a["bs"], 1)), 1)
+    lib = pkvg.library()
+    args = (a["src"], 64, a["bs"], a["entry"], a["bs"] * a["entry"], a["entry"], F, a["T"], dcols, F, width,
+            width, F, 1, None, a["R"])
+    want = lib.gather_cache(args[0], a["kind"], *args[1:], None)
+    info = pkvg.PlanInfo()
+    got = lib.pkvg_plan(RAW, a["kind"], *args, None, ctypes.byref(info))
+    assert got == want != pkvg.PKVG_OK

@@ -6,7 +6,7 @@ compiler's sanitizer runtime:
 - the oracle (plain C, gcc), run through every oracle pin;
 - the C-ABI library with its host code instrumented (hipcc; nothing is
   launched), run through the host-side argument checks of
-  test_capi_host.py.
+  test_capi_host.py and the launch planning of test_plan_host.py.
 
 A planted out-of-bounds call (a destination one row short, handed to the
 oracle) checks that the sanitizer is live in the child.
@@ -116,7 +116,8 @@ def test_host_library_under_sanitizers(tmp_path):
     env = dict(os.environ, LD_PRELOAD=runtime, PKVG_TEST_LIBRARY=out,
                ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                        os.path.join(TESTS, "test_capi_host.py")], cwd=REPO, env=env,
+                        os.path.join(TESTS, "test_capi_host.py"), os.path.join(TESTS, "test_plan_host.py")],
+                       cwd=REPO, env=env,
                        capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
     assert "Sanitizer" not in r.stderr and "runtime error" not in r.stderr, r.stderr[-3000:]
