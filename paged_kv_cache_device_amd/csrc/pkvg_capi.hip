@@ -84,16 +84,17 @@ int64_t max_bytes_stride(int64_t stride, int64_t elem) {
   return stride > INT64_MAX / elem ? -1 : stride * elem;
 }
 
-// Workgroup shape by page size and batch (each choice measured):
-//  * pages of at most 20 KiB of output take the small shape, of at most 36 KiB
-//    the mid one: sized to the page, they fit more pages per CU (2.0-2.5x on
+// Workgroup shape by task-unit size and batch (each choice measured; a unit
+// is a page, a part of one, or a group of pages, as planned below):
+//  * units of at most 20 KiB of output take the small shape, of at most 36 KiB
+//    the mid one: sized to the unit, they fit more units per CU (2.0-2.5x on
 //    16- and 32-token pages);
-//  * larger pages take the wide shape when the batch is found in wave
+//  * larger units take the wide shape when the batch is found in wave
 //    registers or is one request (at most 64 requests) and there are at least
-//    this many page tasks (about four workgroups per CU), or the pages are fp8
+//    this many tasks (about four workgroups per CU), or the pages are fp8
 //    written as one contiguous span (they take the wide shape's store bursts
 //    and write-through stores);
-//  * otherwise the narrow shape (fewer pages, or batches of more than 64
+//  * otherwise the narrow shape (fewer tasks, or batches of more than 64
 //    requests, whose per-workgroup prefix build hides better behind more,
 //    smaller workgroups).
 constexpr int64_t kWideMinTasks = 1024;
