@@ -833,9 +833,8 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
 // kernel's task is instead G = 2^group_shift consecutive logical pages of one
 // request (task_tokens = G * block_size), whose rows are contiguous in the
 // output but scattered in the cache.  Each wave looks the group's G pages up
-// once (lane i holds page i's source offset, -1 when a guard skips it), and
-// every chunk fetches its row's page offset from that lane with a cross-lane
-// read.
+// once (lane i holds page i's physical block, -1 when a guard skips it), and
+// every chunk fetches its row's block from that lane with a cross-lane read.
 
 struct GroupTask {
   int32_t req;
@@ -882,12 +881,13 @@ __device__ __forceinline__ GroupTask resolve_group(const GatherParams& p, const 
   return t;
 }
 
-// One batch of a group: U chunks per lane, chunk c = row c / cpr (row gbeg + c / cpr
-// of the group), column c % cpr.  `lane_phys` is this lane's page of the group
-// (lane < G), -1 when a guard skips it.  Every chunk first finds its row and
-// page, then all chunks fetch their page's block with cross-lane reads, then
-// all loads go out: the phases keep the cross-lane reads from serialising the
-// loads.  As in the page kernel, a lane past the end re-reads the last chunk
+// Moves a group's n chunks in batches of U per lane: chunk c is column c % cpr
+// of the group's row c / cpr, which holds token gbeg + c / cpr counted from the
+// group's first token.  `lane_phys` is the physical block of this lane's page
+// of the group (lane < G), -1 when a guard skips it.  In a batch every chunk
+// first finds its row and page, then all chunks fetch their page's block with
+// cross-lane reads, then all loads go out: the phases keep the cross-lane
+// reads from serialising the loads.  As in the page kernel, a lane past the end re-reads the last chunk
 // and skips its store, and rows of skipped pages read block 0 (it exists
 // whenever some page of the group is valid) and store nothing.
 template <class SH, class M, int LAYOUT>
