@@ -272,6 +272,45 @@ def test_medium_random(seed):
     check_parity(medium_random_workload(seed), DEV)
 
 
+def page_size_random_workload(seed: int) -> workloads.Workload:
+    """A seeded batch over the whole page-size range: block sizes from 1 to
+    1,000 tokens and rows from 1 element to 1,000, so that pages go whole,
+    split into parts or grouped (every task path for each), with every element
+    size, padded rows, seq_starts, clamped and open-ended extents and guard-
+    skipped pages."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    kind = [workloads.RAW, workloads.DEQUANT_FP8, workloads.UPCONVERT, workloads.DEQUANT_AUTO][seed % 4]
+    R = [1, 1, 2, 9, 64, 65, 300, 1100][ri(0, 7)]
+    bs = [1, 2, 3, 4, 5, 7, 8, 16, 24, 64, 96, 128, 256, 1000][ri(0, 13)]
+    entry = [1, 2, 7, 16, 64, 136, 576, 1000][ri(0, 7)]
+    cache_dtype = [torch.bfloat16, torch.float32, torch.uint8][ri(0, 2)]
+    max_tokens = max(24_000 // R, 2)
+    lens = [0 if ri(0, 9) == 0 else ri(1, max_tokens) for _ in range(R)]
+    starts = [ri(0, n // 2) for n in lens] if ri(0, 1) else None
+    pages = sum(-(-n // bs) for n in lens)
+    wl = workloads.make_workload(f"page_size_{seed}", kind, lens, bs, entry, max(pages, 1) + ri(0, 5),
+                                 seed=seed + 31, starts=starts, cache_cols=entry + [0, 0, 1, 3][ri(0, 3)],
+                                 dst_cols=entry + [0, 0, 2, 4][ri(0, 3)], scale=0.05, cache_dtype=cache_dtype)
+    total = int(wl.cu_seq_lens[-1])
+    if ri(0, 4) == 0 and total > 0:
+        T = ri(0, total)
+        wl.num_tokens = T
+        wl.workspace = wl.workspace[: max(T, 1)].clone()
+    if ri(0, 4) == 0:
+        wl = wl.open_ended()
+    if ri(0, 2) == 0 and wl.block_table.numel() > 0:
+        flat = wl.block_table.view(-1)
+        for _ in range(ri(1, 9)):
+            flat[ri(0, flat.numel() - 1)] = [wl.num_blocks, -1, 1 << 29][ri(0, 2)]
+    return wl
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_page_sizes(seed):
+    check_parity(page_size_random_workload(5000 + seed), DEV)
+
+
 # ---------------------------------------------------------------------------
 # the fp8 arithmetic on every code, NaN codes included
 # ---------------------------------------------------------------------------
