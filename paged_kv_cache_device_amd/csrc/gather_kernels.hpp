@@ -218,18 +218,28 @@ __device__ __forceinline__ int64_t request_end(const GatherParams& p, int32_t r)
   return p.num_tokens;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in registers (DPP): four
+// row shifts (row_shr 1, 2, 4, 8; a lane whose source lies before its row of
+// 16 adds 0) give each row's own prefix, then lane 15 of rows 0 and 2 is added
+// into rows 1 and 3 (row_bcast:15) and lane 31 into rows 2 and 3
+// (row_bcast:31).  No LDS round trip, unlike a shuffle.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Exclusive scan over the workgroup; `tmp` holds NWAVES ints of LDS.
 template <int NTHREADS>
 __device__ __forceinline__ int32_t block_exclusive_scan(int32_t x, int32_t* tmp, int32_t& total) {
   constexpr int NW = NTHREADS / 64;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  int32_t incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const int32_t incl = wave_inclusive_scan(x);
   if (lane == 63) tmp[wid] = incl;
   __syncthreads();
   int32_t before = 0;
@@ -273,13 +283,29 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
   const int32_t R = p.num_reqs;
   const int32_t ncu = R + p.cu_terminal;  // entries of cu_seq_lens
   const int32_t lo = static_cast<int32_t>(threadIdx.x) * PER;
+  // Every load is unconditional, at an index clamped into its array (cu has
+  // ncu >= R >= 1 entries, seq_starts R; without seq_starts the cu array
+  // stands in), so all of them are in flight before the first wait; the
+  // values past an array's end are replaced afterwards.
+  const int32_t* starts = p.seq_starts != nullptr ? p.seq_starts : p.cu_seq_lens;
+  int32_t cu_raw[PER + 1];
+  int32_t st_raw[PER];
+#pragma unroll
+  for (int k = 0; k <= PER; ++k) cu_raw[k] = p.cu_seq_lens[min(lo + k, ncu - 1)];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) st_raw[k] = starts[min(lo + k, R - 1)];
+  // used here, before any branch, so no load is sunk behind another's wait
+#pragma unroll
+  for (int k = 0; k <= PER; ++k) asm volatile("" ::"v"(cu_raw[k]));
+#pragma unroll
+  for (int k = 0; k < PER; ++k) asm volatile("" ::"v"(st_raw[k]));
   // cu[lo + k], or num_tokens past the array: request r ends at entry r + 1
   int64_t cuv[PER + 1];
   int32_t st[PER];
 #pragma unroll
-  for (int k = 0; k <= PER; ++k) cuv[k] = lo + k < ncu ? p.cu_seq_lens[lo + k] : p.num_tokens;
+  for (int k = 0; k <= PER; ++k) cuv[k] = lo + k < ncu ? static_cast<int64_t>(cu_raw[k]) : p.num_tokens;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) st[k] = (p.seq_starts != nullptr && lo + k < R) ? p.seq_starts[lo + k] : 0;
+  for (int k = 0; k < PER; ++k) st[k] = (p.seq_starts != nullptr && lo + k < R) ? st_raw[k] : 0;
   int32_t cnt[PER];
   int32_t sum = 0;
 #pragma unroll
@@ -292,6 +318,7 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
       B[lo + k] = static_cast<int32_t>(b);
       S[lo + k] = st[k];
       sum += cnt[k];
+      if (lo + k == R - 1) B[R] = static_cast<int32_t>(e);  // the last request's clamped end
     }
   }
   int32_t total;
@@ -303,10 +330,7 @@ __device__ __forceinline__ void build_prefix_lds(const GatherParams& p, int32_t*
       off += cnt[k];
     }
   }
-  if (threadIdx.x == 0) {
-    P[R] = total;
-    B[R] = static_cast<int32_t>(clamp_rows(request_end(p, R - 1), p.num_tokens));
-  }
+  if (threadIdx.x == 0) P[R] = total;
   __syncthreads();
 }
 
@@ -327,25 +351,28 @@ __device__ __forceinline__ WavePrefix build_prefix_wave(const GatherParams& p) {
   const int lane = threadIdx.x & 63;
   const int32_t R = p.num_reqs;
   WavePrefix w;
-  int64_t cb = 0, ce = 0;
-  int32_t st = 0;
-  if (lane < R) {
-    cb = p.cu_seq_lens[lane];
-    ce = request_end(p, lane);
-    st = p.seq_starts ? p.seq_starts[lane] : 0;
-  }
+  // The three loads are unconditional, at indices clamped into their arrays
+  // (cu_seq_lens has ncu >= R >= 1 entries, seq_starts R; without seq_starts
+  // the cu array stands in), so they share one memory round trip; lanes past
+  // the arrays' ends replace the values afterwards.  Request r ends at entry
+  // r + 1, or at num_tokens when that entry does not exist.
+  const int32_t ncu = R + p.cu_terminal;
+  const int32_t* starts = p.seq_starts ? p.seq_starts : p.cu_seq_lens;
+  const int32_t c0 = p.cu_seq_lens[min(lane, ncu - 1)];
+  const int32_t c1 = p.cu_seq_lens[min(lane + 1, ncu - 1)];
+  const int32_t sv = starts[min(lane, R - 1)];
+  // used here, before any branch, so the compiler cannot sink a load into the
+  // branch that needs it (behind the wait for the others)
+  asm volatile("" ::"v"(c0), "v"(c1), "v"(sv));
+  const int64_t cb = lane < R ? c0 : 0;
+  const int64_t ce = lane < R ? (lane + 1 < ncu ? static_cast<int64_t>(c1) : p.num_tokens) : 0;
   w.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
   w.e = static_cast<int32_t>(clamp_rows(ce, p.num_tokens));
-  w.s = st;
+  w.s = (lane < R && p.seq_starts) ? sv : 0;
   w.count = lane < R ? page_count(p, w.b, w.e, w.s) : 0;
-  int32_t incl = w.count;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const int32_t incl = wave_inclusive_scan(w.count);
   w.incl = incl;
-  w.total = uniform(__shfl(incl, 63, 64));
+  w.total = uniform(__builtin_amdgcn_readlane(incl, 63));
   return w;
 }
 
@@ -704,7 +731,8 @@ __device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSo
   }
   if (ts.mode == kWaveRegs) {
     // the task's request: the number of requests whose inclusive prefix is <= task
-    const int32_t r = uniform(static_cast<int32_t>(__popcll(__ballot(ts.wp.incl <= task))));
+    // (at most R - 1 while task < total; the min keeps every table row in range regardless)
+    const int32_t r = min(uniform(static_cast<int32_t>(__popcll(__ballot(ts.wp.incl <= task)))), p.num_reqs - 1);
     const int32_t b = uniform(__builtin_amdgcn_readlane(ts.wp.b, r));
     const int32_t e = uniform(__builtin_amdgcn_readlane(ts.wp.e, r));
     const int32_t s = uniform(__builtin_amdgcn_readlane(ts.wp.s, r));
@@ -859,7 +887,8 @@ __device__ __forceinline__ GroupTask group_from(int32_t r, const TaskGeom& g) {
 __device__ __forceinline__ GroupTask resolve_group(const GatherParams& p, const TaskSource& ts, int32_t task) {
   if (ts.mode == kSingle) return group_from(0, task_geometry(p, task, ts.b, ts.e, ts.s));
   if (ts.mode == kWaveRegs) {
-    const int32_t r = uniform(static_cast<int32_t>(__popcll(__ballot(ts.wp.incl <= task))));
+    // (at most R - 1 while task < total; the min keeps every table row in range regardless)
+    const int32_t r = min(uniform(static_cast<int32_t>(__popcll(__ballot(ts.wp.incl <= task)))), p.num_reqs - 1);
     const int32_t b = uniform(__builtin_amdgcn_readlane(ts.wp.b, r));
     const int32_t e = uniform(__builtin_amdgcn_readlane(ts.wp.e, r));
     const int32_t s = uniform(__builtin_amdgcn_readlane(ts.wp.s, r));
