@@ -271,9 +271,11 @@ constexpr int64_t kSplitAboveBytes = int64_t(pkvg::Narrow::threads) * pkvg::Narr
 // (8 tokens of 1152-byte rows), which take the small shape.  Measured: the
 // 61,440-token gather on 64-token pages 26.6 -> 25.4 us, the 307,200-token
 // one 120.4 -> 118.9 us, 1,024-token pages 26.0 -> 25.3 us; 18 KiB and 36 KiB
-// units gain less or lose.  Batches lose (every workgroup builds the task
-// prefix: skew-8 +4%, 512 requests +15%) and fp8 pages lose (the 307,200-token
-// upconvert +14%), so both keep the 72 KiB units.
+// units gain less or lose.  So are the raw pages of batches of at most 64
+// requests (wave-register prefix) with fewer whole-page tasks than the wide
+// shape takes: 2, 8 and 64 requests over 61,440 tokens 27.2-27.4 -> 26.7-26.8
+// us.  With more tasks they lose (skew-2/4/8 +0.5-1.5%), and so do larger
+// batches (512 requests +15%) and fp8 pages (the 307,200-token upconvert +14%).
 constexpr int64_t kSplitSingleRawBytes = 9 * 1024;
 
 // Raw pages of batches of more than 64 requests (the LDS-prefix and task-table
@@ -448,9 +450,11 @@ int prepare(int32_t op, int32_t kind, const GatherArgs& a, const float* scale, P
                    a.dst_row_stride, a.block_size);
     if (st != PKVG_OK) return st;
     const int64_t row = int64_t(a.entry) * elem_bytes;
+    // pl.capacity still counts whole pages here
+    const bool small_unit = a.num_reqs == 1 || (a.num_reqs <= pkvg::kWaveMaxReqs && pl.capacity < kWideMinTasks);
     plan_split(pl, row,
-               a.num_reqs == 1 ? kSplitSingleRawBytes
-                               : (a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchRawBytes : kSplitAboveBytes));
+               small_unit ? kSplitSingleRawBytes
+                          : (a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchRawBytes : kSplitAboveBytes));
     plan_group(pl, row);
   } else {
     pl.p.scale = scale;

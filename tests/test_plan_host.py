@@ -75,7 +75,10 @@ def test_headline_gathers():
     (RAW, 2, 96, 1, pkvg.PKVG_KERNEL_PAGES, 6, 4, 0, 256),      # 96 -> 48 -> 24 -> 12 -> 6
     (RAW, 2, 1024, 1, pkvg.PKVG_KERNEL_PAGES, 8, 7, 0, 256),
     (UP, 0, 1024, 1, pkvg.PKVG_KERNEL_PAGES, 64, 4, 0, 1024),   # fp8 keeps 72 KiB units
-    (RAW, 2, 1024, 4, pkvg.PKVG_KERNEL_PAGES, 64, 4, 0, 256),   # small batch: 72 KiB units, < 1024: narrow
+    (RAW, 2, 1024, 4, pkvg.PKVG_KERNEL_PAGES, 8, 7, 0, 256),    # small batch, < 1024 pages: 9 KiB units
+    (RAW, 2, 64, 8, pkvg.PKVG_KERNEL_PAGES, 8, 3, 0, 256),      # 8 x 7,680 tokens: 9 KiB units
+    (RAW, 2, 64, 64, pkvg.PKVG_KERNEL_PAGES, 64, 0, 0, 1024),   # 64 requests: 1,089 tasks, 72 KiB wide
+    (UP, 0, 1024, 4, pkvg.PKVG_KERNEL_PAGES, 64, 4, 0, 1024),   # fp8 small batch: 72 KiB units, wide
     (RAW, 2, 64, 100, pkvg.PKVG_KERNEL_PAGES, 32, 1, 0, 256),   # > 64 requests: 36 KiB units, mid
     (RAW, 2, 127, 1, pkvg.PKVG_KERNEL_PAGES, 127, 0, 0, 256),   # odd: no split, narrow
 ])
