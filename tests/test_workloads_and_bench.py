@@ -67,6 +67,12 @@ def test_named_workload_sizes():
         wl = workloads.named(name)
         assert (wl.num_tokens, wl.block_size, wl.block_table.shape[1]) == (tokens, bs, width), name
         assert wl.algorithmic_bytes() == 2304 * tokens + 4 * (wl.num_reqs + 1), name
+    # the single-60K bytes split evenly over 2, 8 and 64 requests
+    for R in (2, 8, 64):
+        wl = workloads.named(f"batch{R}_60k_raw")
+        assert wl.num_reqs == R and wl.num_tokens == 61440 and wl.seq_starts is None
+        assert wl.context_lens == [61440 // R] * R and wl.num_blocks == 1200
+        assert wl.algorithmic_bytes() == 2304 * 61440 + 4 * (R + 1)
 
 
 def test_bench_refuses_more_than_one_gpu():

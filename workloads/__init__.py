@@ -315,6 +315,14 @@ def batch_raw(R: int, bs: int, seed: int, kind: str = RAW) -> Workload:
     return make_workload(name, kind, [n] * R, bs, 576, R * (-(-n // bs)) + 8, seed=seed, scale=0.0625)
 
 
+def even_batch_60k(R: int, seed: int) -> Workload:
+    """R raw requests sharing the single-60K gather's 61,440 tokens evenly (block 64,
+    entry 576 bf16, 1200 shuffled blocks, no seq_starts).  Not a scenario of the
+    pages: the same bytes as the single-request gather, through the batch task
+    lookup (2 and 8 requests: 9 KiB units; 64 requests: whole pages)."""
+    return make_workload(f"batch{R}_60k_raw", RAW, [61440 // R] * R, 64, 576, 1200, seed=seed)
+
+
 def page_size_single(bs: int, tokens: int, seed: int, kind: str = RAW) -> Workload:
     """One request of `tokens` tokens at block size `bs` (entry 576, shuffled
     blocks): the headline single-request gathers with very small or very large
@@ -349,6 +357,9 @@ NAMED = {
     "single_300k_bs1_fp8_upconvert": lambda: page_size_single(1, 307200, 1202, UPCONVERT),
     "single_60k_bs1024_raw": lambda: page_size_single(1024, 61440, 1203),
     "batch512x200_bs1_raw": lambda: short_batch(512, 200, 1, 1204),
+    "batch2_60k_raw": lambda: even_batch_60k(2, 1301),
+    "batch8_60k_raw": lambda: even_batch_60k(8, 1302),
+    "batch64_60k_raw": lambda: even_batch_60k(64, 1303),
 }
 
 
