@@ -278,13 +278,17 @@ constexpr int64_t kSplitAboveBytes = int64_t(pkvg::Narrow::threads) * pkvg::Narr
 // batches (512 requests +15%) and fp8 pages (the 307,200-token upconvert +14%).
 constexpr int64_t kSplitSingleRawBytes = 9 * 1024;
 
-// Raw pages of batches of more than 64 requests (the LDS-prefix and task-table
-// paths) are split into units of at most 36 KiB (mid shape).  Measured on
-// 64-token pages: 65 x 2000 tokens -6%, 128 x 800 -1.6%, 300 x 3000 -5.5%,
-// 512 x 200 -5%, 1024 x 200 -1.6%, 2048 x 100 -6%; 18 KiB units gain less or
-// lose.  Batches of at most 64 requests (wave-register prefix) lose (skew-8
-// +5%) and fp8 batches gain nothing; both keep 72 KiB units.
-constexpr int64_t kSplitBatchRawBytes = 36 * 1024;
+// Pages of batches of more than 64 requests (the LDS-prefix and task-table
+// paths) are split into units of at most 18 KiB of output (small shape).
+// Raw, on 64-token pages, 36 KiB units against whole pages: 65 x 2000 tokens
+// -6%, 128 x 800 -1.6%, 300 x 3000 -5.5%, 512 x 200 -5%, 1024 x 200 -1.6%,
+// 2048 x 100 -6%; 18 KiB units against 36 KiB (since the LDS prefix costs
+// one round trip): 300 x 3000 -2.7%, 128 x 2000 -1.6%, 512 x 200 -0.5%, and
+// 9 KiB units lose 2-7%.  fp8 to bf16, 18 KiB units against whole pages:
+// 128 x 2000 tokens -4.1%, 512 x 200 -2.8% (9 KiB units lose up to 38%).
+// Batches of at most 64 requests lose with 18 KiB fp8 units (8 x 38,400
+// tokens +2.6%) or 36 KiB raw ones (skew-8 +5%).
+constexpr int64_t kSplitBatchBytes = 18 * 1024;
 
 // Small pages go to the group kernel, whose task is G = 2^k consecutive pages
 // of one request (always the small shape).  Which pages, measured on one
@@ -454,14 +458,14 @@ int prepare(int32_t op, int32_t kind, const GatherArgs& a, const float* scale, P
     const bool small_unit = a.num_reqs == 1 || (a.num_reqs <= pkvg::kWaveMaxReqs && pl.capacity < kWideMinTasks);
     plan_split(pl, row,
                small_unit ? kSplitSingleRawBytes
-                          : (a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchRawBytes : kSplitAboveBytes));
+                          : (a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchBytes : kSplitAboveBytes));
     plan_group(pl, row);
   } else {
     pl.p.scale = scale;
     st = plan_fp8(pl, a.src, a.dst, a.entry, a.src_block_stride, a.src_token_stride, a.dst_row_stride,
                   a.block_size);
     if (st != PKVG_OK) return st;
-    plan_split(pl, 2 * int64_t(a.entry), kSplitAboveBytes);
+    plan_split(pl, 2 * int64_t(a.entry), a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchBytes : kSplitAboveBytes);
     plan_group(pl, 2 * int64_t(a.entry));
   }
   finish_plan(pl);

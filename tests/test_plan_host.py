@@ -79,7 +79,9 @@ def test_headline_gathers():
     (RAW, 2, 64, 8, pkvg.PKVG_KERNEL_PAGES, 8, 3, 0, 256),      # 8 x 7,680 tokens: 9 KiB units
     (RAW, 2, 64, 64, pkvg.PKVG_KERNEL_PAGES, 64, 0, 0, 1024),   # 64 requests: 1,089 tasks, 72 KiB wide
     (UP, 0, 1024, 4, pkvg.PKVG_KERNEL_PAGES, 64, 4, 0, 1024),   # fp8 small batch: 72 KiB units, wide
-    (RAW, 2, 64, 100, pkvg.PKVG_KERNEL_PAGES, 32, 1, 0, 256),   # > 64 requests: 36 KiB units, mid
+    (RAW, 2, 64, 100, pkvg.PKVG_KERNEL_PAGES, 16, 2, 0, 256),   # > 64 requests: 18 KiB units, small
+    (UP, 0, 64, 100, pkvg.PKVG_KERNEL_PAGES, 16, 2, 0, 256),    # ... also for fp8 (18 KiB of bf16)
+    (UP, 0, 64, 64, pkvg.PKVG_KERNEL_PAGES, 64, 0, 0, 1024),    # fp8, <= 64 requests: whole pages, wide
     (RAW, 2, 127, 1, pkvg.PKVG_KERNEL_PAGES, 127, 0, 0, 256),   # odd: no split, narrow
 ])
 def test_task_units_and_kernels(op, kind, bs, R, kernel, tokens, split, group, threads):
