@@ -300,12 +300,14 @@ constexpr int64_t kSplitBatchBytes = 18 * 1024;
 // each build the task prefix for one small page).  So: pages of at most
 // 4.5 KiB of output always, of at most 9 KiB for batches and fp8.
 // How many: the largest G <= 64 whose pages hold at most 9 KiB of output (one
-// request, raw), 20 KiB (one request, fp8) or 36 KiB (batches).  Against 20 KiB
+// request, raw), 20 KiB (one request, fp8) or 18 KiB (batches).  Against 20 KiB
 // groups, one request's raw 1- and 2-token pages take 1.8% less time in 9 KiB
-// groups (its fp8 pages 4% more), and 512-request batches 1.5% less in 36 KiB
-// groups (single requests 5% more).
+// groups (its fp8 pages 4% more).  Batches against 36 KiB groups: 512 x 200
+// one-token pages -5.7% (fp8 -2%), 8 x 7,680 and 64 x 960 one-token pages
+// -4%, 128 x 2000 four-token pages -5%; 9 KiB groups lose 1-40%.
 constexpr int64_t kGroupMaxPageBytes = 4608;
 constexpr int64_t kGroupMaxPageBytesBatchOrFp8 = 9216;
+constexpr int64_t kGroupBatchBytes = 18 * 1024;
 constexpr int32_t kMaxGroupShift = 6;
 
 void plan_group(Plan& pl, int64_t row_out_bytes) {
@@ -315,7 +317,7 @@ void plan_group(Plan& pl, int64_t row_out_bytes) {
   const bool batch_or_fp8 = pl.p.num_reqs > 1 || pl.convert == pkvg::kFp8Bf16;
   if (page_out > (batch_or_fp8 ? kGroupMaxPageBytesBatchOrFp8 : kGroupMaxPageBytes)) return;
   const int64_t max_group_bytes =
-      pl.p.num_reqs > 1 ? kMidMaxPageBytes : (pl.convert == pkvg::kFp8Bf16 ? kSmallMaxPageBytes : kSplitSingleRawBytes);
+      pl.p.num_reqs > 1 ? kGroupBatchBytes : (pl.convert == pkvg::kFp8Bf16 ? kSmallMaxPageBytes : kSplitSingleRawBytes);
   int32_t k = 0;
   while (k < kMaxGroupShift && (page_out << (k + 1)) <= max_group_bytes) ++k;
   if (k == 0) return;

@@ -66,11 +66,11 @@ def test_headline_gathers():
 @pytest.mark.parametrize("op,kind,bs,R,kernel,tokens,split,group,threads", [
     (RAW, 2, 1, 1, pkvg.PKVG_KERNEL_GROUPS, 8, 0, 3, 256),      # 9 KiB groups of one-token pages
     (UP, 0, 1, 1, pkvg.PKVG_KERNEL_GROUPS, 16, 0, 4, 256),      # 18 KiB groups (fp8)
-    (RAW, 2, 1, 512, pkvg.PKVG_KERNEL_GROUPS, 32, 0, 5, 256),   # 36 KiB groups (batch)
+    (RAW, 2, 1, 512, pkvg.PKVG_KERNEL_GROUPS, 16, 0, 4, 256),   # 18 KiB groups (batch)
     (RAW, 2, 3, 1, pkvg.PKVG_KERNEL_GROUPS, 6, 0, 1, 256),      # 3-token pages in pairs
     (RAW, 2, 8, 1, pkvg.PKVG_KERNEL_PAGES, 8, 0, 0, 256),       # 9 KiB pages: one per workgroup
     (UP, 0, 8, 1, pkvg.PKVG_KERNEL_GROUPS, 16, 0, 1, 256),      # ... but grouped for fp8
-    (RAW, 2, 8, 70, pkvg.PKVG_KERNEL_GROUPS, 32, 0, 2, 256),    # ... and for batches
+    (RAW, 2, 8, 70, pkvg.PKVG_KERNEL_GROUPS, 16, 0, 1, 256),    # ... and for batches (pairs)
     (RAW, 2, 16, 1, pkvg.PKVG_KERNEL_PAGES, 8, 1, 0, 256),      # one request: 8-token units
     (RAW, 2, 96, 1, pkvg.PKVG_KERNEL_PAGES, 6, 4, 0, 256),      # 96 -> 48 -> 24 -> 12 -> 6
     (RAW, 2, 1024, 1, pkvg.PKVG_KERNEL_PAGES, 8, 7, 0, 256),
