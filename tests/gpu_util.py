@@ -62,3 +62,24 @@ def check_parity(wl: workloads.Workload, device: str = "cuda:0") -> None:
     got = ws.cpu()
     same = torch.equal(got.view(torch.uint8), want.view(torch.uint8))
     assert same, f"{wl.name}: " + byte_diff(got, want)
+
+
+def plan_of(wl_dev: workloads.Workload) -> dict:
+    """How the library would run ``wl_dev``'s call (pkvg_plan with the same
+    marshalled arguments as the call), so a test can check which path it took."""
+    g = wl_dev
+    dst = g.workspace[: g.num_tokens, : g.entry]
+    common = (g.src_cache(), dst, g.block_table, g.cu_seq_lens, g.num_reqs)
+    if g.kind == workloads.RAW:
+        a = pkvg.prepare("gather_cache", *common, g.seq_starts)._args
+        op, kind, cache, scale = pkvg.PKVG_OP_GATHER_CACHE, a[1], a[2:17], None
+    elif g.kind in (workloads.DEQUANT_AUTO, workloads.DEQUANT_FP8):
+        fp8 = g.kind == workloads.DEQUANT_FP8
+        a = pkvg.prepare("gather_maybe_dequant", *common, "fp8" if fp8 else "auto",
+                         scale=g.scale_tensor if fp8 else None, seq_starts=g.seq_starts)._args
+        op, kind, cache, scale = pkvg.PKVG_OP_GATHER_MAYBE_DEQUANT, a[1], a[2:17], a[17]
+    else:
+        a = pkvg.prepare("gather_upconvert_fp8", *common, g.scale_tensor,
+                         seq_starts=g.seq_starts)._args
+        op, kind, cache, scale = pkvg.PKVG_OP_GATHER_UPCONVERT_FP8, 0, a[1:16], a[16]
+    return pkvg.pkvg_plan(op, kind, a[0], *cache, scale)

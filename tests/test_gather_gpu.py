@@ -9,8 +9,9 @@ import torch
 
 import oracle
 import oracle_pins
+import paged_kv_cache_device_amd as pkvg
 import workloads
-from gpu_util import byte_diff, check_parity, log, run_hip
+from gpu_util import byte_diff, check_parity, log, plan_of, run_hip
 
 pytestmark = pytest.mark.gpu
 
@@ -309,6 +310,44 @@ def page_size_random_workload(seed: int) -> workloads.Workload:
 @pytest.mark.parametrize("seed", range(40))
 def test_random_page_sizes(seed):
     check_parity(page_size_random_workload(5000 + seed), DEV)
+
+
+# ---------------------------------------------------------------------------
+# task-unit rules by batch size, each case pinned to its plan, with seq_starts,
+# zero-length requests, partial pages and guard-skipped pages
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,kind,R,bs,mode,unit,split,group", [
+    # at most 64 requests and fewer than 1024 whole-page tasks: raw 9 KiB units
+    ("small_batch_raw", workloads.RAW, 8, 64, "wave", 8, 3, 0),
+    ("small_batch_raw_big_pages", workloads.RAW, 5, 1024, "wave", 8, 7, 0),
+    # ... fp8 keeps whole pages
+    ("small_batch_fp8", workloads.UPCONVERT, 8, 64, "wave", 64, 0, 0),
+    # more than 64 requests: 18 KiB units, raw and fp8 (LDS prefix and task table)
+    ("lds_batch_raw", workloads.RAW, 65, 64, "lds", 16, 2, 0),
+    ("lds_batch_fp8", workloads.DEQUANT_FP8, 200, 64, "lds", 16, 2, 0),
+    ("table_batch_fp8", workloads.UPCONVERT, 1100, 64, "table", 16, 2, 0),
+    # small pages of batches: 18 KiB groups
+    ("lds_batch_groups", workloads.RAW, 300, 1, "lds", 16, 0, 4),
+    ("wave_batch_groups", workloads.RAW, 20, 2, "wave", 16, 0, 3),
+])
+def test_batch_unit_rules(name, kind, R, bs, mode, unit, split, group):
+    g = torch.Generator("cpu").manual_seed(len(name) * 1000 + R)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    max_tokens = max(30_000 // R, 40)
+    lens = [0 if ri(0, 7) == 0 else ri(1, max_tokens) for _ in range(R)]
+    starts = [ri(0, n // 3) for n in lens]
+    pages = sum(-(-n // bs) for n in lens)
+    wl = workloads.make_workload(name, kind, lens, bs, 576, pages + 7, seed=R + bs, starts=starts,
+                                 scale=0.05)
+    flat = wl.block_table.view(-1)
+    for _ in range(5):  # guard-skipped pages: past the cache, negative
+        flat[ri(0, flat.numel() - 1)] = [wl.num_blocks, -1][ri(0, 1)]
+    p = plan_of(wl.to(DEV))
+    modes = {"wave": pkvg.PKVG_TASKS_WAVE, "lds": pkvg.PKVG_TASKS_LDS, "table": pkvg.PKVG_TASKS_TABLE}
+    assert (p["task_mode"], p["task_tokens"], p["split_shift"], p["group_shift"]) == (
+        modes[mode], unit, split, group), p
+    check_parity(wl, DEV)
 
 
 # ---------------------------------------------------------------------------
