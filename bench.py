@@ -339,8 +339,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the gather "
-              "shards by request or page range with no exchange, and multi-GPU runs are "
-              "not part of this build", file=sys.stderr)
+              "shards by request or page range with no exchange; this benchmark measures "
+              "one GPU's share and does not launch several", file=sys.stderr)
         sys.exit(2)
 
     import torch
