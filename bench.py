@@ -311,6 +311,30 @@ def host_threads() -> int:
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
+# --kind of a custom workload -> the workload kind (entry point and conversion)
+CUSTOM_KINDS = {"raw": "raw", "fp8_upconvert": "upconvert", "fp8_dequant": "dequant_fp8",
+                "auto": "dequant_auto"}
+
+
+def custom_workload_name(args) -> str:
+    lens = [int(x) for x in args.lens.split(",")]
+    return (f"custom_{args.kind}_R{len(lens)}_T{sum(lens)}_bs{args.block_size}_e{args.entry}"
+            f"{'_starts' if args.starts else ''}")
+
+
+def custom_workload(args):
+    """A workload from the command line: the given context lengths, block size and
+    entry, shuffled physical blocks (5/4 of the pages needed), seeded values."""
+    import workloads
+
+    lens = [int(x) for x in args.lens.split(",")]
+    pages = sum(-(-n // args.block_size) for n in lens)
+    return workloads.make_workload(custom_workload_name(args), CUSTOM_KINDS[args.kind], lens,
+                                   args.block_size, args.entry, max(pages * 5 // 4, 1) + 8,
+                                   seed=args.seed, draw_starts_quarter=args.starts,
+                                   scale=args.scale)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,7 +353,20 @@ def main():
     ap.add_argument("--counter-command", default="",
                     help="with --summarize-counters: the profiling command, stored verbatim")
     ap.add_argument("--cold-reps", type=int, default=100)
+    custom = ap.add_argument_group(
+        "custom workload", "instead of --workload: one built from these flags (seeded, shuffled blocks)")
+    custom.add_argument("--lens", help="comma-separated context lengths, one per request")
+    custom.add_argument("--kind", default="raw", choices=sorted(CUSTOM_KINDS),
+                        help="raw copy, fp8 upconvert, fp8 dequant, or 'auto' (bf16 copy)")
+    custom.add_argument("--block-size", type=int, default=64)
+    custom.add_argument("--entry", type=int, default=576, help="elements gathered per token")
+    custom.add_argument("--starts", action="store_true",
+                        help="seq_starts drawn uniformly from [0, len / 4]")
+    custom.add_argument("--scale", type=float, default=0.0625, help="fp8 per-tensor scale")
+    custom.add_argument("--seed", type=int, default=1)
     args = ap.parse_args()
+    if args.lens:
+        args.workload = custom_workload_name(args)
 
     if args.summarize_counters:
         res = summarize_counters(args.summarize_counters, args.workload, args.calibration_copy_mib,
@@ -351,7 +388,7 @@ def main():
     pkvg.library()
     dev = torch.device("cuda:0")
     log(f"[bench] workload {args.workload}: generating")
-    wl = workloads.named(args.workload)
+    wl = custom_workload(args) if args.lens else workloads.named(args.workload)
     g = wl.to(dev)
     alg_bytes = wl.algorithmic_bytes()
     sets = make_sets(g, 3 << 30)  # far above the 256 MB Infinity Cache
@@ -402,8 +439,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # raw gathers copy bytes; the fp8 paths decode and scale in fp32
-        "dtype": "u8" if wl.kind == workloads.RAW else "f32",
+        # raw and 'auto' gathers copy bytes; the fp8 paths decode and scale in fp32
+        "dtype": "u8" if wl.kind in (workloads.RAW, workloads.DEQUANT_AUTO) else "f32",
         "data": "synthetic (seeded N(0,1) bf16 / uniform non-NaN e4m3fn codes; shuffled blocks)",
         "config": {"workload": wl.name, "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
                    "block_size": wl.block_size, "entry": wl.entry,

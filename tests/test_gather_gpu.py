@@ -350,6 +350,15 @@ def test_batch_unit_rules(name, kind, R, bs, mode, unit, split, group):
     check_parity(wl, DEV)
 
 
+@pytest.mark.parametrize("block", range(10))
+def test_random_sweep(block):
+    """Both random generators above at 15 more seeds per block (300 cases in
+    all): every task path, unit rule, access width and edge case, many times."""
+    for seed in range(20000 + 15 * block, 20000 + 15 * (block + 1)):
+        check_parity(medium_random_workload(seed), DEV)
+        check_parity(page_size_random_workload(seed), DEV)
+
+
 # ---------------------------------------------------------------------------
 # the fp8 arithmetic on every code, NaN codes included
 # ---------------------------------------------------------------------------

@@ -130,3 +130,25 @@ def test_threaded_oracle_baseline_matches_oracle(name, parts):
     with ThreadPoolExecutor(max_workers=2) as pool:
         bench.oracle_threaded(open_wl, 3, ws)(pool)
     assert torch.equal(ws.view(torch.uint8), want.view(torch.uint8))
+
+
+@pytest.mark.parametrize("kind", ["raw", "fp8_upconvert", "fp8_dequant", "auto"])
+def test_bench_custom_workload(kind):
+    """bench.py --lens/--kind/--block-size/--entry/--starts builds a seeded
+    workload of exactly that shape, with the library kind of that name."""
+    import argparse
+
+    sys.path.insert(0, REPO)
+    import bench
+
+    ns = argparse.Namespace(lens="300,0,77", kind=kind, block_size=16, entry=64, starts=True,
+                            scale=0.05, seed=5)
+    wl = bench.custom_workload(ns)
+    want_kind = {"raw": workloads.RAW, "fp8_upconvert": workloads.UPCONVERT,
+                 "fp8_dequant": workloads.DEQUANT_FP8, "auto": workloads.DEQUANT_AUTO}[kind]
+    assert wl.kind == want_kind and wl.name == bench.custom_workload_name(ns)
+    assert wl.context_lens == [300, 0, 77] and (wl.block_size, wl.entry) == (16, 64)
+    starts = wl.seq_starts.tolist()
+    assert all(0 <= s <= n // 4 for s, n in zip(starts, [300, 0, 77]))
+    assert wl.num_tokens == sum(n - s for n, s in zip([300, 0, 77], starts))
+    assert wl.num_blocks >= 19 + 5
