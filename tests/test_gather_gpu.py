@@ -47,10 +47,12 @@ def test_random_small_workloads(seed):
         check_parity(wl, DEV)
 
 
-@pytest.mark.parametrize("R,bs", [(64, 16), (300, 16), (1024, 4), (1025, 4), (3000, 2)])
+@pytest.mark.parametrize("R,bs", [(64, 16), (300, 16), (1024, 4), (1025, 4), (3000, 2), (20000, 1),
+                                  (70000, 2)])
 def test_many_requests(R, bs):
     """Fused builder with several requests per thread (R > 256), the largest fused
-    batch, and the tabled builder beyond it."""
+    batch, and the tabled builder beyond it (its scan carries across up to 69
+    chunks of 1024 requests; one-token pages go through the group kernel)."""
     g = torch.Generator("cpu").manual_seed(R)
     lens = torch.randint(0, 5 * bs, (R,), generator=g)
     lens[torch.rand(R, generator=g) < 0.15] = 0
