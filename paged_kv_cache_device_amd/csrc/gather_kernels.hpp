@@ -751,6 +751,20 @@ __device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSo
                    static_cast<int64_t>(uniform(t.out_begin)));
 }
 
+// The task mode of a launch (low byte of the mode argument).  Each kernel is
+// built twice: for one request, where the mode is the constant kSingle and the
+// other modes' code drops out, and for batches, where the compiler is told it
+// is never kSingle.  Measured on one request against a single build for all
+// modes: 61,440 tokens on 64-token pages 25.2 -> 25.05 us, on 1,024-token
+// pages 25.14 -> 24.92 us.
+template <bool ONE_REQUEST>
+__device__ __forceinline__ int task_mode_of(int32_t mode_arg) {
+  if constexpr (ONE_REQUEST) return kSingle;
+  const int mode = mode_arg & 0xFF;
+  __builtin_assume(mode != kSingle);
+  return mode;
+}
+
 // One int32 read through the vector memory path.  Its wait (vmcnt) leaves the
 // scalar loads in flight alone: scalar loads complete in any order, so waiting
 // for one scalar load waits for all of them, kernel arguments included.
@@ -770,7 +784,7 @@ __device__ __forceinline__ int32_t load_i32_vector_path(const int32_t* q) {
 // scalars are preloaded into SGPRs when a wave starts (gfx950 kernarg
 // preloading), so the metadata loads go out without waiting for a kernel
 // argument fetch; the struct arrives while they are in flight.
-template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, bool ONE_REQUEST>
 __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
     const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
     int32_t mode_and_split, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
@@ -792,7 +806,7 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
 
   const int32_t R = p.num_reqs;
   TaskSource ts;
-  ts.mode = mode_and_split & 0xFF;
+  ts.mode = task_mode_of<ONE_REQUEST>(mode_and_split);
   int32_t* P = lds;
   int32_t* B = lds + (R + 1);
   int32_t* S = lds + 2 * (R + 1);
@@ -965,7 +979,7 @@ __device__ __forceinline__ void move_group(const GatherParams& p, int32_t lane_p
 // arguments; `mode_and_group` holds the TaskMode (low byte) and group_shift
 // (the byte above it).  Loads always use flat (row-relative) chunk addressing:
 // each row is addressed on its own.
-template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, bool ONE_REQUEST>
 __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
     const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
     int32_t mode_and_group, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
@@ -990,7 +1004,7 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
   const int32_t G = 1 << p.group_shift;
   const int32_t R = p.num_reqs;
   TaskSource ts;
-  ts.mode = mode_and_group & 0xFF;
+  ts.mode = task_mode_of<ONE_REQUEST>(mode_and_group);
   int32_t* P = lds;
   int32_t* B = lds + (R + 1);
   int32_t* S = lds + 2 * (R + 1);

@@ -118,18 +118,26 @@ int32_t task_mode(const GatherParams& p) {
   return p.num_reqs <= pkvg::kWaveMaxReqs ? pkvg::kWaveRegs : pkvg::kLdsPrefix;
 }
 
+// Each kernel has a build for one request and one for batches (the task mode
+// is then a constant, or known not to be kSingle).
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_shape(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  return launch(pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC>, grid, SH::threads, lds, stream,
-                p.cu_seq_lens, p.block_table, p.seq_starts, task_mode(p) | (p.split_shift << 8), p.num_reqs,
-                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens, p);
+  const int32_t mode = task_mode(p);
+  auto kernel = mode == pkvg::kSingle ? pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, true>
+                                      : pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, false>;
+  return launch(kernel, grid, SH::threads, lds, stream, p.cu_seq_lens, p.block_table, p.seq_starts,
+                mode | (p.split_shift << 8), p.num_reqs, p.task_tokens, p.task_tokens_magic,
+                p.block_table_width, p.cu_terminal, p.num_tokens, p);
 }
 
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_groups(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  return launch(pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC>, grid, SH::threads, lds, stream,
-                p.cu_seq_lens, p.block_table, p.seq_starts, task_mode(p) | (p.group_shift << 8), p.num_reqs,
-                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens, p);
+  const int32_t mode = task_mode(p);
+  auto kernel = mode == pkvg::kSingle ? pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, true>
+                                      : pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, false>;
+  return launch(kernel, grid, SH::threads, lds, stream, p.cu_seq_lens, p.block_table, p.seq_starts,
+                mode | (p.group_shift << 8), p.num_reqs, p.task_tokens, p.task_tokens_magic,
+                p.block_table_width, p.cu_terminal, p.num_tokens, p);
 }
 
 // The workgroup shape of a plan (the rules above; the group kernel always
