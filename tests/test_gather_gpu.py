@@ -352,6 +352,26 @@ def test_batch_unit_rules(name, kind, R, bs, mode, unit, split, group):
     check_parity(wl, DEV)
 
 
+@pytest.mark.parametrize("R", [256, 257, 512, 513])
+@pytest.mark.parametrize("kind", [workloads.RAW, workloads.UPCONVERT])
+def test_lds_prefix_share_boundaries(R, kind):
+    """The LDS prefix gives each of a workgroup's 256 lanes 1, 2 or 4 requests,
+    the smallest share that covers the batch: batches on both sides of each
+    switch, with seq_starts, zero-length requests and guard-skipped pages."""
+    g = torch.Generator("cpu").manual_seed(R * 10 + len(kind))
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    lens = [0 if ri(0, 6) == 0 else ri(1, 300) for _ in range(R)]
+    starts = [ri(0, n // 3) for n in lens]
+    pages = sum(-(-n // 16) for n in lens)
+    wl = workloads.make_workload(f"lds_share_{R}_{kind}", kind, lens, 16, 576, pages + 5, seed=R,
+                                 starts=starts, scale=0.05)
+    flat = wl.block_table.view(-1)
+    for _ in range(4):
+        flat[ri(0, flat.numel() - 1)] = [wl.num_blocks, -1][ri(0, 1)]
+    assert plan_of(wl.to(DEV))["task_mode"] == pkvg.PKVG_TASKS_LDS
+    check_parity(wl, DEV)
+
+
 @pytest.mark.parametrize("block", range(10))
 def test_random_sweep(block):
     """Both random generators above at 15 more seeds per block (300 cases in
