@@ -364,23 +364,44 @@ struct WavePrefix {
   int32_t total;  // all tasks (uniform)
 };
 
-__device__ __forceinline__ WavePrefix build_prefix_wave(const GatherParams& p) {
+// The wave prefix's metadata: this lane's cu_seq_lens entry, the next one and
+// its seq_start.  The three loads are unconditional, at indices clamped into
+// their arrays (cu_seq_lens has ncu >= R >= 1 entries, seq_starts R; without
+// seq_starts the cu array stands in), so they share one memory round trip;
+// build_prefix_wave replaces the values of lanes past the arrays' ends.  The
+// batch builds issue them first thing, ahead of the task-mode branches: where
+// the other modes' code joins the path in front of them, the compiler waits
+// for every outstanding scalar load (the parameter struct's fetch among them)
+// before they go out.  Measured: 8 x 7,680 one-token pages 27.84 -> 27.49 us;
+// the page kernel's batches unchanged.
+struct WaveLoads {
+  int32_t c0, c1, sv;
+};
+
+__device__ __forceinline__ WaveLoads issue_wave_loads(const GatherParams& p) {
+  const int lane = threadIdx.x & 63;
+  const int32_t R = p.num_reqs;
+  const int32_t ncu = R + p.cu_terminal;
+  const int32_t* starts = p.seq_starts ? p.seq_starts : p.cu_seq_lens;
+  WaveLoads l;
+  l.c0 = p.cu_seq_lens[min(lane, ncu - 1)];
+  l.c1 = p.cu_seq_lens[min(lane + 1, ncu - 1)];
+  l.sv = starts[min(lane, R - 1)];
+  // used here, so the compiler cannot sink a load into a later branch (behind
+  // the wait for the others)
+  asm volatile("" ::"v"(l.c0), "v"(l.c1), "v"(l.sv));
+  return l;
+}
+
+// Request r ends at entry r + 1, or at num_tokens when that entry does not exist.
+
+__device__ __forceinline__ WavePrefix build_prefix_wave(const GatherParams& p, const WaveLoads& l) {
   const int lane = threadIdx.x & 63;
   const int32_t R = p.num_reqs;
   WavePrefix w;
-  // The three loads are unconditional, at indices clamped into their arrays
-  // (cu_seq_lens has ncu >= R >= 1 entries, seq_starts R; without seq_starts
-  // the cu array stands in), so they share one memory round trip; lanes past
-  // the arrays' ends replace the values afterwards.  Request r ends at entry
-  // r + 1, or at num_tokens when that entry does not exist.
+  // lanes past the arrays' ends replace the loaded values
   const int32_t ncu = R + p.cu_terminal;
-  const int32_t* starts = p.seq_starts ? p.seq_starts : p.cu_seq_lens;
-  const int32_t c0 = p.cu_seq_lens[min(lane, ncu - 1)];
-  const int32_t c1 = p.cu_seq_lens[min(lane + 1, ncu - 1)];
-  const int32_t sv = starts[min(lane, R - 1)];
-  // used here, before any branch, so the compiler cannot sink a load into the
-  // branch that needs it (behind the wait for the others)
-  asm volatile("" ::"v"(c0), "v"(c1), "v"(sv));
+  const int32_t c0 = l.c0, c1 = l.c1, sv = l.sv;
   const int64_t cb = lane < R ? c0 : 0;
   const int64_t ce = lane < R ? (lane + 1 < ncu ? static_cast<int64_t>(c1) : p.num_tokens) : 0;
   w.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
@@ -824,6 +845,10 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
   const int32_t R = p.num_reqs;
   TaskSource ts;
   ts.mode = task_mode_of<ONE_REQUEST>(mode_and_split);
+  WaveLoads wave_loads{};
+  if constexpr (!ONE_REQUEST) {
+    if (ts.mode == kWaveRegs) wave_loads = issue_wave_loads(p);
+  }
   int32_t* P = lds;
   int32_t* B = lds + (R + 1);
   int32_t* S = lds + 2 * (R + 1);
@@ -858,7 +883,7 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
     ts.e = static_cast<int32_t>(clamp_rows(p.cu_terminal ? ce : p.num_tokens, p.num_tokens));
     num_tasks = page_count(p, ts.b, ts.e, ts.s);
   } else if (ts.mode == kWaveRegs) {
-    ts.wp = build_prefix_wave(p);
+    ts.wp = build_prefix_wave(p, wave_loads);
     num_tasks = ts.wp.total;
   } else if (ts.mode == kLdsPrefix) {
     build_prefix_lds_for<SH::threads>(p, P, B, S, scan_tmp);
@@ -1022,6 +1047,10 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
   const int32_t R = p.num_reqs;
   TaskSource ts;
   ts.mode = task_mode_of<ONE_REQUEST>(mode_and_group);
+  WaveLoads wave_loads{};
+  if constexpr (!ONE_REQUEST) {
+    if (ts.mode == kWaveRegs) wave_loads = issue_wave_loads(p);
+  }
   int32_t* P = lds;
   int32_t* B = lds + (R + 1);
   int32_t* S = lds + 2 * (R + 1);
@@ -1046,7 +1075,7 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
     ts.e = static_cast<int32_t>(clamp_rows(p.cu_terminal ? ce : p.num_tokens, p.num_tokens));
     num_tasks = page_count(p, ts.b, ts.e, ts.s);
   } else if (ts.mode == kWaveRegs) {
-    ts.wp = build_prefix_wave(p);
+    ts.wp = build_prefix_wave(p, wave_loads);
     num_tasks = ts.wp.total;
   } else if (ts.mode == kLdsPrefix) {
     build_prefix_lds_for<SH::threads>(p, P, B, S, scan_tmp);
