@@ -180,20 +180,30 @@ int64_t oracle_gather(int32_t mode,
  * ------------------------------------------------------------------------ */
 
 /*
- * The page's task map (section "implementation breakdown", step 1, and the
- * GatherPageTask / map_gather_page_task snippet): tasks are numbered request
- * by request; request r contributes one task per logical page its source
- * range [s, s+n) touches, counted as ceil((s+n)/bs) - floor(s/bs) pages.  A
- * task records (req_id, logical_block, page_token_begin, page_token_end,
- * output_token_begin): the copied slots [begin, end) of that logical page
- * relative to the page start, and the output row of the first copied slot.
- * b and n are the clamped output extent used by oracle_gather.
+ * The page-task decomposition (section "implementation breakdown", step 1, and
+ * the GatherPageTask fields of section "key source snippets"): a task is one
+ * logical page of one request together with the run of that request's
+ * gathered tokens that lie on it.
  *
- * Note that this count gives one task with an empty slot range when n == 0
- * and s is not a multiple of bs; the page's method launches such a task and
- * it copies nothing.  Tasks are written five int32 at a time into out (room
- * for cap tasks); the return value is the total number of tasks, which may
- * exceed cap (then only the first cap are written).
+ * Defined here straight from the per-token gather above.  The tokens of each
+ * request are visited in output order, as oracle_gather visits them: output
+ * row b + i takes source token t = s + i, which lies in slot t % block_size of
+ * logical page t / block_size.  Consecutive tokens of one request that share
+ * a logical page belong to one task; a token whose (request, logical page)
+ * pair differs from the previous token's opens the next task.  A task
+ * records (req_id, logical_block, page_token_begin, page_token_end,
+ * output_token_begin): the slot of its first token, one past the slot of its
+ * last token, and the output row of its first token.  Tasks are numbered in
+ * the order they open (request by request, page by page).
+ *
+ * A request that gathers no rows has no tokens and therefore no task.  The
+ * page's own count of pages per request gives such a request one task with an
+ * empty slot range when its start is not a multiple of block_size; that task
+ * copies nothing, so both readings give the same gather.
+ *
+ * Tasks are written five int32 at a time into out (room for cap tasks); the
+ * return value is the total number of tasks, which may exceed cap (then only
+ * the first cap are written).
  */
 int64_t oracle_page_tasks(const int32_t *cu_seq_lens, int32_t terminal, const int32_t *seq_starts,
                           int32_t num_reqs, int64_t num_tokens, int32_t block_size,
@@ -205,21 +215,25 @@ int64_t oracle_page_tasks(const int32_t *cu_seq_lens, int32_t terminal, const in
         int64_t e = min64(request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal), num_tokens);
         int64_t n = max64(e - b, 0);
         int64_t s = seq_starts ? seq_starts[r] : 0;
-        int64_t first_page = s / block_size;
-        int64_t end_page = (s + n + block_size - 1) / block_size; /* ceil */
-        for (int64_t lb = first_page; lb < end_page; ++lb) {
-            int64_t page_begin = lb * block_size;
-            int64_t copy_begin = max64(s, page_begin);
-            int64_t copy_end = min64(s + n, page_begin + block_size);
-            if (count < cap) {
-                int32_t *task = out + 5 * count;
-                task[0] = r;
-                task[1] = (int32_t)lb;
-                task[2] = (int32_t)(copy_begin - page_begin);
-                task[3] = (int32_t)(copy_end - page_begin);
-                task[4] = (int32_t)(b + copy_begin - s);
+        int64_t open_page = -1; /* logical page of the task the previous token joined */
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t t = s + i;
+            int64_t page = t / block_size;
+            int64_t slot = t % block_size;
+            if (page != open_page) {
+                open_page = page;
+                if (count < cap) {
+                    int32_t *task = out + 5 * count;
+                    task[0] = r;
+                    task[1] = (int32_t)page;
+                    task[2] = (int32_t)slot;
+                    task[3] = (int32_t)(slot + 1);
+                    task[4] = (int32_t)(b + i);
+                }
+                ++count;
+            } else if (count <= cap) {
+                out[5 * (count - 1) + 3] = (int32_t)(slot + 1);
             }
-            ++count;
         }
     }
     return count;

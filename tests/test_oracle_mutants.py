@@ -17,7 +17,9 @@ import oracle
 # output): dropping the clamp of a request's first output row (a begin past
 # num_tokens already gives an empty extent through the clamped end), and
 # rounding the decoded code to bf16 before scaling (an e4m3fn value has at most
-# 4 significant bits, so that rounding is exact).
+# 4 significant bits, so that rounding is exact); and opening a task at slot 0
+# instead of on a change of logical page (a request's tokens are consecutive,
+# so after its first token the two coincide).
 MUTANTS = [
     ("slot off by one", "int64_t slot = t % block_size;", "int64_t slot = (t + 1) % block_size;", 0),
     ("logical block off by one", "int64_t logical = t / block_size;",
@@ -53,11 +55,12 @@ MUTANTS = [
      "double p = (double)oracle_e4m3fn_to_f32(code) * (double)scale; int ex;\n"
      "    double q = ldexp(nearbyint(frexp(p, &ex) * 256.0) / 256.0, ex);\n"
      "    volatile float product = (float)q;", 0),
-    ("page count uses floor", "(s + n + block_size - 1) / block_size", "(s + n) / block_size", 0),
-    ("task output row relative to the page", "task[4] = (int32_t)(b + copy_begin - s);",
-     "task[4] = (int32_t)(b + copy_begin - page_begin);", 0),
-    ("task end relative to the copy begin", "task[3] = (int32_t)(copy_end - page_begin);",
-     "task[3] = (int32_t)(copy_end - copy_begin);", 0),
+    ("task page from the output row", "int64_t page = t / block_size;",
+     "int64_t page = (b + i) / block_size;", 0),
+    ("task end never extended", "out[5 * (count - 1) + 3] = (int32_t)(slot + 1);", ";", 0),
+    ("task output row relative to the page", "task[4] = (int32_t)(b + i);",
+     "task[4] = (int32_t)(b + slot);", 0),
+    ("task begin slot off by one", "task[2] = (int32_t)slot;", "task[2] = (int32_t)(slot + 1);", 0),
     ("task map ignores seq_starts", "int64_t s = seq_starts ? seq_starts[r] : 0;",
      "int64_t s = 0;", 1),
     ("task end not clamped to num_tokens",
