@@ -2,16 +2,23 @@
 
 One step = one call of the library on one batch (all of the hot path: page-task
 build, block lookup, page copy / dequant), inputs already resident in HBM.
-Default workload: one request of 61,440 tokens (960 pages of 64), 576 bf16 per
-token, shuffled physical blocks, raw copy.  Metric: effective HBM GB/s
-(algorithmic bytes read + written per step / time per step).
+Headline workload: one request of 307,200 tokens (4,800 pages of 64), 576 fp8
+e4m3fn codes per token upconverted to bf16 with a per-tensor scale, shuffled
+physical blocks.  The same run also times the second single-request gather
+(61,440 bf16 tokens, raw copy) with the same steps and warmup and reports it
+as a nested object.  Metric: effective HBM GB/s (algorithmic bytes read +
+written per step / time per step).
 
-Cold-cache measurement: the timed steps rotate over several copies of the
+Timing: exactly K back-to-back calls bracketed by torch.cuda.synchronize(),
+with one HIP event pair on the launch stream around them.  `value` and
+`ms_per_step` come from the events (the GPU time of the K calls);
+`wall_ms_per_step` is the host clock over the same bracket, which adds the two
+synchronisation latencies.  The timed steps rotate over several copies of the
 inputs and outputs whose total is far above the 256 MB Infinity Cache, so no
 step finds its data in a cache.  Printed on stdout: ONE JSON line.  Progress
 goes to stderr.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAME]
 """
 from __future__ import annotations
 
@@ -29,7 +36,8 @@ sys.path.insert(0, REPO)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
 METRIC = "effective HBM GB/s (read+write) and % of peak; median gather latency, 1 GPU"
-DEFAULT_WORKLOAD = "single_60k_raw"
+DEFAULT_WORKLOAD = "single_300k_fp8_upconvert"
+SECOND_WORKLOAD = "single_60k_raw"
 TRAFFIC_DIR = os.path.join(REPO, "profiles")
 KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp",
                   "paged_kv_cache_device_amd/csrc/pkvg_capi.hip"]
@@ -311,6 +319,53 @@ def host_threads() -> int:
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
+def measure(wl, dev, args) -> dict:
+    """Time `args.steps` calls of workload `wl` (cold by rotation), then a warm
+    run and single calls after a cache scrub; returns the numbers of one bench
+    line (rates from the event-timed region, see the module docstring)."""
+    import torch
+
+    import workloads
+
+    g = wl.to(dev)
+    alg_bytes = wl.algorithmic_bytes()
+    sets = make_sets(g, 3 << 30)  # far above the 256 MB Infinity Cache
+    log(f"[bench] {wl.name}: {len(sets)} input/output copies; algorithmic bytes/step {alg_bytes}")
+    wall, ev_ms = time_steps(sets, args.steps, args.warmup)
+    kern_ms = ev_ms / args.steps
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"[bench] {wl.name}: {args.steps} steps: {kern_ms * 1e3:.2f} us/launch (events), "
+        f"{wall / args.steps * 1e6:.2f} us/step wall, {achieved:.0f} GB/s")
+    _, ev_w = time_steps(sets[:1], args.steps, args.warmup)
+    warm_us = ev_w / args.steps * 1e3
+    del sets
+    cold = cold_latency(g, args.cold_reps)
+    log(f"[bench] {wl.name}: cold scrubbed median {cold['median_us']:.2f} us; warm {warm_us:.2f} us")
+    torch.cuda.empty_cache()
+    return {
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(kern_ms, 6),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 6),
+        # raw and 'auto' gathers copy bytes; the fp8 paths decode and scale in fp32
+        "dtype": "u8" if wl.kind in (workloads.RAW, workloads.DEQUANT_AUTO) else "f32",
+        "config": {"workload": wl.name, "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
+                   "block_size": wl.block_size, "entry": wl.entry,
+                   "num_blocks": wl.num_blocks, "kind": wl.kind,
+                   "algorithmic_bytes_per_step": alg_bytes,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
+        "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
+        "per_launch_us": round(kern_ms * 1e3, 3),
+        "latency_us": {"cold_scrubbed_single_call": {k: round(v, 3) for k, v in cold.items()},
+                       "back_to_back_per_launch_cold": round(kern_ms * 1e3, 3),
+                       "back_to_back_per_launch_warm": round(warm_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(wl.name)},
+    }
+
+
 # --kind of a custom workload -> the workload kind (entry point and conversion)
 CUSTOM_KINDS = {"raw": "raw", "fp8_upconvert": "upconvert", "fp8_dequant": "dequant_fp8",
                 "auto": "dequant_auto"}
@@ -341,6 +396,9 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default=SECOND_WORKLOAD,
+                    help="a second named workload timed in the same run and reported as a "
+                         "nested object ('' for none)")
     ap.add_argument("--only-gather", action="store_true",
                     help="run warmup + steps of the gather and nothing else (for profilers)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -389,14 +447,12 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] workload {args.workload}: generating")
     wl = custom_workload(args) if args.lens else workloads.named(args.workload)
-    g = wl.to(dev)
-    alg_bytes = wl.algorithmic_bytes()
-    sets = make_sets(g, 3 << 30)  # far above the 256 MB Infinity Cache
-    log(f"[bench] {len(sets)} input/output copies; algorithmic bytes/step {alg_bytes}")
 
     if args.only_gather:
+        sets = make_sets(wl.to(dev), 3 << 30)  # far above the 256 MB Infinity Cache
         wall, _ = time_steps(sets, args.steps, args.warmup)
         log(f"[bench] only-gather: {args.steps} steps in {wall * 1e3:.2f} ms")
+        del sets
         if args.calibration_copy_mib:
             n = args.calibration_copy_mib << 20
             bufs = [(torch.empty(n, dtype=torch.uint8, device=dev),
@@ -408,54 +464,36 @@ def main():
             log(f"[bench] calibration: 10 copies of {n} bytes")
         return
 
-    # the timed region: exactly `steps` calls; HIP events on the launch stream
-    # around the region give the average launch duration for the roofline
-    wall, ev_ms = time_steps(sets, args.steps, args.warmup)
-    ms_per_step = wall / args.steps * 1e3
-    value = alg_bytes / (wall / args.steps) / 1e9
-    kern_ms = ev_ms / args.steps
-    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step wall, "
-        f"{kern_ms * 1e3:.2f} us/launch (events), {value:.0f} GB/s")
-
-    # warm (the same buffers back to back) and single calls after a cache scrub
-    _, ev_w = time_steps(sets[:1], args.steps, args.warmup)
-    warm_us = ev_w / args.steps * 1e3
-    cold = cold_latency(g, args.cold_reps)
-    log(f"[bench] cold scrubbed median {cold['median_us']:.2f} us; warm {warm_us:.2f} us")
+    head = measure(wl, dev, args)
     payload_each_way = wl.gathered_rows() * wl.entry * wl.dst_elem_bytes
     copy_ref = copy_reference(payload_each_way, dev, args.steps, 3 << 30)
     log(f"[bench] device copy reference {copy_ref['gbs']:.0f} GB/s")
+    also = None
+    if args.also and args.also != wl.name and not args.lens:
+        log(f"[bench] second workload {args.also}: generating")
+        also = measure(workloads.named(args.also), dev, args)
+        torch.cuda.empty_cache()
 
-    traffic = measured_traffic(args.workload)
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # raw and 'auto' gathers copy bytes; the fp8 paths decode and scale in fp32
-        "dtype": "u8" if wl.kind in (workloads.RAW, workloads.DEQUANT_AUTO) else "f32",
+        "dtype": head["dtype"],
         "data": "synthetic (seeded N(0,1) bf16 / uniform non-NaN e4m3fn codes; shuffled blocks)",
-        "config": {"workload": wl.name, "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
-                   "block_size": wl.block_size, "entry": wl.entry,
-                   "num_blocks": wl.num_blocks, "kind": wl.kind,
-                   "algorithmic_bytes_per_step": alg_bytes,
-                   "parallelism": "single GPU"},
-        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
-        "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
-        "per_launch_us": round(kern_ms * 1e3, 3),
-        "latency_us": {"cold_scrubbed_single_call": {k: round(v, 3) for k, v in cold.items()},
-                       "back_to_back_per_launch_cold": round(kern_ms * 1e3, 3),
-                       "back_to_back_per_launch_warm": round(warm_us, 3)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic},
+        "config": head["config"],
+        "pct_of_peak": head["pct_of_peak"],
+        "wall_ms_per_step": head["wall_ms_per_step"],
+        "median_latency_us_cold_scrubbed": head["median_latency_us_cold_scrubbed"],
+        "per_launch_us": head["per_launch_us"],
+        "latency_us": head["latency_us"],
+        "roofline": head["roofline"],
         "copy_reference": copy_ref,
         # the pages' own figures (their page kernel against the prior kernel, kernel latency,
         # on another vendor's GPU): relative context only, nothing here reproduces them
@@ -464,6 +502,8 @@ def main():
                                                          "maybe_dequant": "1.39-1.77"},
                     "pages_dram_fraction_of_peak": "0.75-0.84"},
     }
+    if also is not None:
+        result[also["config"]["workload"]] = also
     if not args.no_cpu:
         n = host_threads()
         log(f"[bench] timing the CPU oracle: {n} threads, then one (about 8 s each)")

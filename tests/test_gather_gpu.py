@@ -37,6 +37,27 @@ def test_named_workload_parity(name):
 
 
 # ---------------------------------------------------------------------------
+# the page's own kernel test shape: 17 / 32,768 / 71 rows, starts 3 / 17 / 5,
+# block 64, entry 576, each table row a permutation of all 1,024 blocks
+# ---------------------------------------------------------------------------
+
+PAGES_TEST_CALLS = [
+    (workloads.RAW, torch.bfloat16),        # gather_cache, 'auto' (bf16) cache
+    (workloads.RAW, torch.uint8),           # gather_cache, one-byte fp8 cache copied as bytes
+    (workloads.DEQUANT_AUTO, torch.bfloat16),
+    (workloads.DEQUANT_FP8, None),
+    (workloads.UPCONVERT, None),
+]
+
+
+@pytest.mark.parametrize("use_starts", [False, True])
+@pytest.mark.parametrize("kind,cache_dtype", PAGES_TEST_CALLS,
+                         ids=["raw_bf16", "raw_u8", "auto", "fp8", "upconvert"])
+def test_pages_large_uneven_sequences(kind, cache_dtype, use_starts):
+    check_parity(workloads.pages_uneven_test(kind, use_starts, cache_dtype or torch.bfloat16), DEV)
+
+
+# ---------------------------------------------------------------------------
 # random small workloads: partial pages, seq_starts, zero-length requests,
 # aliased blocks, strided rows, num_tokens clamping, guard-skipped pages
 # ---------------------------------------------------------------------------

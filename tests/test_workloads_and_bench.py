@@ -152,3 +152,28 @@ def test_bench_custom_workload(kind):
     assert all(0 <= s <= n // 4 for s, n in zip(starts, [300, 0, 77]))
     assert wl.num_tokens == sum(n - s for n, s in zip([300, 0, 77], starts))
     assert wl.num_blocks >= 19 + 5
+
+
+@pytest.mark.parametrize("use_starts", [False, True])
+def test_pages_uneven_test_shape(use_starts):
+    """The page's own kernel-test case: 17 / 32,768 / 71 gathered rows, starts
+    3 / 17 / 5, block 64, entry 576, 1,024 blocks, every table row a full
+    permutation of the blocks (rows alias)."""
+    wl = workloads.pages_uneven_test(workloads.RAW, use_starts)
+    assert wl.cu_seq_lens.tolist() == [0, 17, 17 + 32768, 17 + 32768 + 71]
+    assert (wl.block_size, wl.entry, wl.num_blocks) == (64, 576, 1024)
+    assert tuple(wl.block_table.shape) == (3, 1024)
+    for r in range(3):
+        assert sorted(wl.block_table[r].tolist()) == list(range(1024))
+    assert (wl.seq_starts.tolist() if use_starts else None) == ([3, 17, 5] if use_starts else None)
+    u8 = workloads.pages_uneven_test(workloads.RAW, use_starts, torch.uint8)
+    assert u8.cache_base.dtype == torch.uint8 and u8.workspace.dtype == torch.uint8
+
+
+def test_bench_defaults_name_both_single_request_gathers():
+    sys.path.insert(0, REPO)
+    import bench
+
+    assert bench.DEFAULT_WORKLOAD == "single_300k_fp8_upconvert"
+    assert bench.SECOND_WORKLOAD == "single_60k_raw"
+    assert set(workloads.NAMED) >= {bench.DEFAULT_WORKLOAD, bench.SECOND_WORKLOAD}

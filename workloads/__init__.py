@@ -147,16 +147,24 @@ def bf16_normal(gen: torch.Generator, shape) -> torch.Tensor:
 
 
 def deal_block_table(gen: torch.Generator, context_lens, block_size: int, num_blocks: int,
-                     width: Optional[int] = None, allow_alias: bool = False) -> torch.Tensor:
+                     width: Optional[int] = None, allow_alias: bool = False,
+                     full_rows: bool = False) -> torch.Tensor:
     """int32 [R, W]: distinct physical blocks from one randperm, -1 in unused slots.
 
     With ``allow_alias`` each row is an independent ``randperm`` prefix, so rows
-    may share physical blocks (legal: the gather only reads the cache).
+    may share physical blocks (legal: the gather only reads the cache).  With
+    ``full_rows`` every row is the first W entries of its own
+    ``randperm(num_blocks)``: rows alias and no slot is unused.
     """
     pages = [-(-int(n) // block_size) for n in context_lens]
     W = max(pages + [1]) if width is None else width
     assert W >= max(pages + [0])
     bt = torch.full((len(context_lens), W), -1, dtype=torch.int32)
+    if full_rows:
+        assert W <= num_blocks
+        for r in range(len(context_lens)):
+            bt[r] = torch.randperm(num_blocks, generator=gen)[:W].to(torch.int32)
+        return bt
     if allow_alias:
         for r, p in enumerate(pages):
             assert p <= num_blocks
@@ -184,7 +192,7 @@ def make_workload(name: str, kind: str, context_lens, block_size: int, entry: in
                   workspace_rows: Optional[int] = None, num_tokens: Optional[int] = None,
                   scale: float = 1.0, gen: Optional[torch.Generator] = None,
                   allow_alias: bool = False, draw_starts_quarter: bool = False,
-                  cache_dtype: torch.dtype = torch.bfloat16) -> Workload:
+                  cache_dtype: torch.dtype = torch.bfloat16, full_rows: bool = False) -> Workload:
     """Build one workload.  ``starts``: explicit list, or None; with
     ``draw_starts_quarter`` each start is drawn uniformly from [0, len // 4].
     ``cache_dtype`` (raw kinds only): bf16 / fp32 values from N(0,1), or uint8
@@ -197,7 +205,8 @@ def make_workload(name: str, kind: str, context_lens, block_size: int, entry: in
     if draw_starts_quarter:
         starts = [int(torch.randint(0, n // 4 + 1, (1,), generator=gen).item())
                   for n in context_lens]
-    bt = deal_block_table(gen, context_lens, block_size, num_blocks, width, allow_alias)
+    bt = deal_block_table(gen, context_lens, block_size, num_blocks, width, allow_alias,
+                          full_rows)
     cache_cols = entry if cache_cols is None else cache_cols
     dst_cols = entry if dst_cols is None else dst_cols
     cshape = (num_blocks, block_size, cache_cols)
@@ -304,6 +313,28 @@ def mixed_dequant_strided() -> Workload:
     return make_workload("mixed_fp8_dequant_strided", DEQUANT_FP8, lens, 64, 576, nb, seed=1005,
                          gen=gen, cache_cols=577, dst_cols=580, scale=0.05,
                          workspace_rows=sum(lens) + 16)
+
+
+# The uneven batch of the page's own kernel test (page 1, "key source
+# snippets", test_cp_gather_cache_mla_large_uneven_sequences): 17, 32,768 and
+# 71 gathered tokens, starts 3, 17 and 5 when seq_starts are used, block 64,
+# entry 576, 1,024 physical blocks, every block-table row its own random
+# permutation of all 1,024 blocks.
+PAGES_TEST_ROWS = [17, 32768, 71]
+PAGES_TEST_STARTS = [3, 17, 5]
+
+
+def pages_uneven_test(kind: str, use_starts: bool, cache_dtype: torch.dtype = torch.bfloat16,
+                      seed: int = 1401) -> Workload:
+    """The page's large-uneven-sequences test case for one entry point: ``kind``
+    picks the call; for RAW, ``cache_dtype`` bf16 is its 'auto' cache and uint8
+    its one-byte fp8 cache copied as bytes."""
+    starts = PAGES_TEST_STARTS if use_starts else None
+    lens = [n + (s if use_starts else 0) for n, s in zip(PAGES_TEST_ROWS, PAGES_TEST_STARTS)]
+    tag = {torch.bfloat16: "bf16", torch.uint8: "u8"}[cache_dtype] if kind == RAW else kind
+    return make_workload(f"pages_uneven_{tag}{'_starts' if use_starts else ''}", kind, lens, 64,
+                         576, 1024, seed=seed, starts=starts, width=1024, full_rows=True,
+                         cache_dtype=cache_dtype, scale=0.0625)
 
 
 def batch_raw(R: int, bs: int, seed: int, kind: str = RAW) -> Workload:
