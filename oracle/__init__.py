@@ -71,6 +71,9 @@ class Oracle:
         lib.oracle_gather.restype = i64
         lib.oracle_page_tasks.argtypes = [vp, i32, vp, i32, i64, i32, vp, i64]
         lib.oracle_page_tasks.restype = i64
+        lib.oracle_indexer_gather.argtypes = [vp, i64, i32, i64, i32, i32, i32, i32, vp, i64, vp,
+                                              i64, i64, vp, vp, i32, vp, i32, i64]
+        lib.oracle_indexer_gather.restype = i64
         self.lib = lib
         self.path = path
 
@@ -125,6 +128,26 @@ class Oracle:
         self.lib.oracle_page_tasks(_ptr(cu), int(terminal), _ptr(ss), num_reqs, num_tokens,
                                    block_size, _ptr(out), count)
         return out[:count]
+
+    def indexer_gather(self, cache: np.ndarray, num_blocks: int, block_size: int,
+                       block_stride: int, layout: int, head_dim: int, block_tile: int,
+                       head_tile: int, dst_values: np.ndarray, dst_value_stride: int,
+                       dst_scales: np.ndarray, dst_scale_stride: int, num_tokens: int,
+                       token_to_seq, cu_seqlen, num_batches: int, block_table,
+                       block_table_width: int, block_table_ld: int) -> int:
+        """Indexer quant-cache gather into ``dst_values`` / ``dst_scales`` (flat
+        uint8 arrays, in place); strides in bytes.  Returns rows written."""
+        for a in (cache, dst_values, dst_scales):
+            assert a.dtype == np.uint8 and a.flags["C_CONTIGUOUS"]
+        t2s = _as_i32(token_to_seq)
+        cu = _as_i32(cu_seqlen)
+        bt = _as_i32(block_table)
+        assert t2s.size >= num_tokens
+        return int(self.lib.oracle_indexer_gather(
+            _ptr(cache), num_blocks, block_size, block_stride, layout, head_dim, block_tile,
+            head_tile, _ptr(dst_values), dst_value_stride, _ptr(dst_scales), dst_scale_stride,
+            num_tokens, _ptr(t2s), _ptr(cu), num_batches, _ptr(bt), block_table_width,
+            block_table_ld))
 
     def gather_tensors(self, mode: int, src_cache, dst, block_table, cu_seq_lens, seq_starts,
                        num_reqs: int, scale: float = 1.0, terminal: bool = True) -> int:
@@ -182,3 +205,22 @@ def run_workload(wl, ws=None):
     rows = o.gather_tensors(mode, wl.src_cache(), dst_view, wl.block_table, wl.cu_seq_lens,
                             wl.seq_starts, wl.num_reqs, wl.scale, wl.cu_terminal)
     return ws, rows
+
+
+def run_indexer_workload(iw, values=None, scales=None):
+    """Oracle indexer gather for a ``workloads.IndexerWorkload`` on CPU into the
+    destinations ``values`` / ``scales`` (default: fresh sentinel-filled ones).
+    Returns (values, scales, rows written)."""
+    import torch
+
+    o = load()
+    values = iw.fresh_values() if values is None else values
+    scales = iw.fresh_scales() if scales is None else scales
+    assert values.is_contiguous() and scales.is_contiguous()
+    rows = o.indexer_gather(
+        iw.cache.numpy().reshape(-1), iw.num_blocks, iw.block_size, iw.block_stride, iw.layout,
+        iw.head_dim, iw.block_tile, iw.head_tile, values.numpy().reshape(-1), values.stride(0),
+        scales.view(torch.uint8).numpy().reshape(-1), 4 * scales.stride(0), iw.num_tokens,
+        iw.token_to_seq.numpy(), iw.cu_seqlen.numpy(), iw.num_batches,
+        iw.block_table.numpy(), iw.block_table_width, iw.block_table.shape[1])
+    return values, scales, rows

@@ -9,8 +9,11 @@
  *
  * Source of the method: the prhub.com.cn summary of vLLM pull request 51739,
  * "MLA cache gather scheduled by logical page; raw copy up to 331x faster"
- * (page 1 of the reference pages).  Every function cites the passage it
- * follows.  Where that page is silent the readings taken are stated inline.
+ * (page 1 of the reference pages), and for the indexer quant-cache gather at
+ * the end of this file the summary of pull request 56153, "indexer kernel
+ * takes runtime arguments; no per-shape recompiles" (page 3).  Every function
+ * cites the passage it follows.  Where a page is silent the readings taken
+ * are stated inline.
  *
  * Every function here is pinned by a CPU test against something other than
  * itself (a hand-worked case, a library cast, a closed form, or an
@@ -237,4 +240,98 @@ int64_t oracle_page_tasks(const int32_t *cu_seq_lens, int32_t terminal, const in
         }
     }
     return count;
+}
+
+/* ------------------------------------------------------------------------
+ * The indexer quant-cache gather
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Source: the prhub.com.cn summary of vLLM pull request 56153, "indexer
+ * kernel takes runtime arguments; no per-shape recompiles" (page 3 of the
+ * reference pages), section "key source snippets" (the masks and the
+ * clamp-then-widen block addressing of _cp_gather_indexer_quant_cache_kernel)
+ * and section "implementation breakdown", steps 2-4 (which values are
+ * structural constants and which are runtime bounds, used only in the masks).
+ *
+ * One program per output row tid: the row belongs to batch (sequence)
+ * token_to_seq[tid]; the batch's rows are [cu_seqlen[b], cu_seqlen[b + 1]).
+ * The snippet shows the masks on tid, on the batch id, on the block-table
+ * column and the in-block offset, and on the physical block id, then the
+ * block id clamped to 0 when invalid and only then widened to 64 bits.  It
+ * elides the index arithmetic in between and the packed cache layout; the
+ * readings taken here:
+ *
+ *  - valid_token: the batch is valid and batch_start <= tid < batch_end; the
+ *    row's position in its sequence is pos = tid - batch_start.
+ *  - block_table_id = pos / block_size, block_offset = pos % block_size,
+ *    block_table_offset = b * block_table_ld + block_table_id.
+ *  - Packed block record (block_stride bytes per physical block): the values
+ *    of the block's block_size tokens (head_dim fp8 bytes each) first, then
+ *    one fp32 scale per token (4 bytes each, token order) at byte
+ *    block_size * head_dim.  LAYOUT picks how the value bytes are ordered:
+ *      0 (flat):  token o, byte d at o * head_dim + d;
+ *      1 (tiled): the value area is cut into tiles of block_tile tokens by
+ *                 head_tile bytes, stored tile after tile: tile rows
+ *                 (o / block_tile) outermost, then tile columns
+ *                 (d / head_tile), and inside a tile token-major, i.e.
+ *                 ((o / bt) * (head_dim / ht) + d / ht) * bt * ht
+ *                   + (o % bt) * ht + d % ht.
+ *  - A row whose mask is false is left untouched (masked stores); a valid
+ *    row gets the token's head_dim value bytes in dst_values[tid] and its 4
+ *    scale bytes in dst_scales[tid], both copied bit for bit.
+ *
+ * Strides: block_stride and dst_value_stride in bytes, dst_scale_stride in
+ * bytes too (the HIP boundary takes it in fp32 elements).  Returns the number
+ * of rows written.
+ */
+int64_t oracle_indexer_gather(const uint8_t *cache, int64_t num_blocks, int32_t block_size,
+                              int64_t block_stride, int32_t layout, int32_t head_dim,
+                              int32_t block_tile, int32_t head_tile,
+                              uint8_t *dst_values, int64_t dst_value_stride,
+                              uint8_t *dst_scales, int64_t dst_scale_stride,
+                              int64_t num_tokens, const int32_t *token_to_seq,
+                              const int32_t *cu_seqlen, int32_t num_batches,
+                              const int32_t *block_table, int32_t block_table_width,
+                              int64_t block_table_ld)
+{
+    int64_t rows_written = 0;
+    for (int64_t tid = 0; tid < num_tokens; ++tid) {
+        /* the batch of this row, and its rows [batch_start, batch_end) */
+        int64_t batch = token_to_seq[tid];
+        if (batch < 0 || batch >= num_batches)
+            continue;
+        int64_t batch_start = cu_seqlen[batch];
+        int64_t batch_end = cu_seqlen[batch + 1];
+        if (tid < batch_start || tid >= batch_end)
+            continue;
+        /* position in the sequence -> block-table column and slot */
+        int64_t pos = tid - batch_start;
+        int64_t block_table_id = pos / block_size;
+        int64_t block_offset = pos % block_size;
+        if (block_table_id < 0 || block_table_id >= block_table_width ||
+            block_offset < 0 || block_offset >= block_size)
+            continue;
+        int64_t block_id = block_table[batch * block_table_ld + block_table_id];
+        if (block_id < 0 || block_id >= num_blocks)
+            continue;
+        /* the block id is valid here, so clamping is a no-op; widen before the multiply */
+        const uint8_t *record = cache + block_id * block_stride;
+        uint8_t *out = dst_values + tid * dst_value_stride;
+        for (int32_t d = 0; d < head_dim; ++d) {
+            int64_t at;
+            if (layout == 0) {
+                at = block_offset * head_dim + d;
+            } else {
+                int64_t tile = (block_offset / block_tile) * (head_dim / head_tile) + d / head_tile;
+                at = tile * block_tile * head_tile + (block_offset % block_tile) * head_tile +
+                     d % head_tile;
+            }
+            out[d] = record[at];
+        }
+        const uint8_t *scale = record + (int64_t)block_size * head_dim + block_offset * 4;
+        memcpy(dst_scales + tid * dst_scale_stride, scale, 4);
+        ++rows_written;
+    }
+    return rows_written;
 }

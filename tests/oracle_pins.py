@@ -499,6 +499,115 @@ def check_page_task_coverage(o, seed=14, count=200):
         assert all(pend > pbeg for _, _, pbeg, pend, _ in tasks.tolist())
 
 
+# ---------------------------------------------------------------------------
+# the indexer quant-cache gather
+# ---------------------------------------------------------------------------
+
+def check_indexer_hand_worked(o):
+    g = _golden("indexer_hand_worked.json")
+    nb, bs, hd, stride = g["num_blocks"], g["block_size"], g["head_dim"], g["block_stride"]
+    cache = (np.arange(nb * stride) % 256).astype(np.uint8)  # block k byte i = 16k + i
+    T = len(g["token_to_seq"])
+    vs, ss = g["dst_value_stride"], g["dst_scale_stride_bytes"]
+    bt = np.array(g["block_table"], dtype=np.int32)
+    for case in g["cases"]:
+        vals = np.full(T * vs, g["sentinel"], dtype=np.uint8)
+        scal = np.full(T * ss, g["sentinel"], dtype=np.uint8)
+        rows = o.indexer_gather(cache, nb, bs, stride, case["layout"], hd, case["block_tile"],
+                                case["head_tile"], vals, vs, scal, ss, T, g["token_to_seq"],
+                                g["cu_seqlen"], g["num_batches"], bt, case["block_table_width"],
+                                bt.shape[1])
+        assert rows == sum(v is not None for v in case["values"]), case["why"]
+        for t in range(T):
+            want_v = case["values"][t] or [g["sentinel"]] * hd
+            want_s = case["scales"][t] or [g["sentinel"]] * 4
+            assert vals[t * vs: t * vs + hd].tolist() == want_v, (case["why"], t)
+            assert scal[t * ss: t * ss + 4].tolist() == want_s, (case["why"], t)
+            # the pad byte of each value row and the second scale slot stay untouched
+            assert vals[t * vs + hd] == g["sentinel"] and (scal[t * ss + 4:(t + 1) * ss] == 255).all()
+
+
+def pack_indexer_records(values: np.ndarray, scales: np.ndarray, layout: int, block_tile: int,
+                         head_tile: int, pad: int) -> np.ndarray:
+    """Pack logical per-token values [NB, bs, D] (bytes) and scales [NB, bs, 4]
+    (bytes) into block records: the value area (token-major, or tile after tile
+    for the tiled layout, by numpy reshape/transpose), then the scales, then
+    `pad` zero bytes."""
+    nb, bs, hd = values.shape
+    if layout == workloads.INDEXER_LAYOUT_FLAT:
+        area = values.reshape(nb, bs * hd)
+    else:
+        t = values.reshape(nb, bs // block_tile, block_tile, hd // head_tile, head_tile)
+        area = t.transpose(0, 1, 3, 2, 4).reshape(nb, bs * hd)
+    return np.ascontiguousarray(np.concatenate(
+        [area, scales.reshape(nb, bs * 4), np.zeros((nb, pad), dtype=np.uint8)], axis=1))
+
+
+def check_indexer_vs_logical_tensors(o, seed=21, count=80):
+    """Random indexer gathers on caches packed from logical value / scale
+    tensors (both layouts, several tile shapes); the expected rows come from
+    indexing the logical tensors with masks for the batch id, the row range,
+    the table width and the block id, computed over all rows at once."""
+    rng = np.random.default_rng(seed)
+    for k in range(count):
+        B = int(rng.integers(1, 6))
+        bs = int(rng.choice([2, 4, 8, 16, 32]))
+        hd = int(rng.choice([16, 32, 64]))
+        layout = k % 2
+        bt_, ht_ = (int(rng.choice([t for t in (1, 2, 4, 8, 16) if bs % t == 0])),
+                    int(rng.choice([t for t in (1, 2, 4, 8, 16) if hd % t == 0])))
+        lens = rng.integers(0, 4 * bs + 3, size=B)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        T = int(cu[-1]) + int(rng.integers(0, 4))
+        t2s = np.full(T, -1, dtype=np.int64)
+        for b in range(B):
+            t2s[cu[b]:cu[b + 1]] = b
+        # corruptions: padding ids, ids past the batch count, rows claiming another batch
+        for _ in range(int(rng.integers(0, 4))):
+            if T:
+                t2s[int(rng.integers(0, T))] = int(rng.choice([-1, -5, B, B + 3, int(rng.integers(0, B))]))
+        # a batch's first row claiming the previous batch, just past that batch's rows
+        for b in range(1, B):
+            if lens[b] and rng.random() < 0.5:
+                t2s[cu[b]] = b - 1
+        W = max(int(-(-lens.max() // bs)), 1)
+        width = W if rng.random() < 0.7 else int(rng.integers(0, W + 1))
+        ld = W + int(rng.integers(0, 3))
+        nb = int(rng.integers(1, 3 * W + 2))
+        # one more batch in the arrays than num_batches: ids >= B must not reach it
+        table = rng.integers(-2, nb + 2, size=(B + 1, ld)).astype(np.int32)
+        cu_arr = np.concatenate([cu, [cu[-1] + T + 1]])
+        vals = rng.integers(0, 256, size=(nb, bs, hd), dtype=np.uint8)
+        scl = rng.integers(0, 256, size=(nb, bs, 4), dtype=np.uint8)
+        pad = int(rng.choice([0, 4, 16]))
+        cache = pack_indexer_records(vals, scl, layout, bt_, ht_, pad)
+        stride = cache.shape[1]
+        vs, ss = hd + int(rng.integers(0, 3)), 4 * int(rng.integers(1, 3))
+        got_v = np.full((T, vs), 0xAB, dtype=np.uint8)
+        got_s = np.full((T, ss), 0xCD, dtype=np.uint8)
+        rows = o.indexer_gather(cache.reshape(-1), nb, bs, stride, layout, hd, bt_, ht_,
+                                got_v.reshape(-1), vs, got_s.reshape(-1), ss, T,
+                                t2s.astype(np.int32), cu_arr.astype(np.int32), B, table, width, ld)
+        # expected, all rows at once
+        tid = np.arange(T)
+        ok = (t2s >= 0) & (t2s < B)
+        b = np.where(ok, t2s, 0)
+        start, end = cu[b], cu[b + 1]
+        ok &= (tid >= start) & (tid < end)
+        pos = np.where(ok, tid - start, 0)
+        col, off = pos // bs, pos % bs
+        ok &= col < width
+        blk = np.where(ok, table[b, np.minimum(col, ld - 1)], -1)
+        ok &= (blk >= 0) & (blk < nb)
+        want_v = np.full((T, vs), 0xAB, dtype=np.uint8)
+        want_s = np.full((T, ss), 0xCD, dtype=np.uint8)
+        want_v[ok, :hd] = vals[blk[ok], off[ok]]
+        want_s[ok, :4] = scl[blk[ok], off[ok]]
+        assert rows == int(ok.sum()), k
+        assert np.array_equal(got_v, want_v), (k, layout, bs, hd, bt_, ht_)
+        assert np.array_equal(got_s, want_s), (k, layout, bs, hd)
+
+
 ALL_CHECKS = [
     check_decode_spec_values, check_decode_matches_torch, check_bf16_hand,
     check_bf16_matches_torch, check_dequant_worked, check_dequant_matches_torch,
@@ -506,4 +615,5 @@ ALL_CHECKS = [
     check_gather_fp8_hand_worked,
     check_gather_vs_torch_indexing, check_gather_vs_page_method,
     check_self_identifying_invariants, check_page_task_closed_forms, check_page_task_coverage,
+    check_indexer_hand_worked, check_indexer_vs_logical_tensors,
 ]

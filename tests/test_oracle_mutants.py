@@ -63,6 +63,27 @@ MUTANTS = [
     ("task begin slot off by one", "task[2] = (int32_t)slot;", "task[2] = (int32_t)(slot + 1);", 0),
     ("task map ignores seq_starts", "int64_t s = seq_starts ? seq_starts[r] : 0;",
      "int64_t s = 0;", 1),
+    ("indexer position ignores the batch start", "int64_t pos = tid - batch_start;",
+     "int64_t pos = tid;", 0),
+    ("indexer row range check dropped",
+     "if (tid < batch_start || tid >= batch_end)\n            continue;", "", 0),
+    ("indexer batch upper bound dropped", "if (batch < 0 || batch >= num_batches)",
+     "if (batch < 0)", 0),
+    ("indexer table width guard dropped", "block_table_id >= block_table_width ||", "", 0),
+    ("indexer block id upper guard off by one", "block_id >= num_blocks", "block_id > num_blocks", 0),
+    ("indexer negative block id guard dropped", "block_id < 0 || ", "", 0),
+    ("indexer table pitch uses the width", "batch * block_table_ld", "batch * block_table_width", 0),
+    ("indexer tiles ordered column-major",
+     "(block_offset / block_tile) * (head_dim / head_tile) + d / head_tile",
+     "(d / head_tile) * (block_size / block_tile) + block_offset / block_tile", 0),
+    ("indexer tile interior byte-major",
+     "(block_offset % block_tile) * head_tile +\n                     d % head_tile",
+     "(d % head_tile) * block_tile +\n                     block_offset % block_tile", 0),
+    ("indexer flat values ignore the slot", "at = block_offset * head_dim + d;", "at = d;", 0),
+    ("indexer scales at the record start",
+     "record + (int64_t)block_size * head_dim + block_offset * 4", "record + block_offset * 4", 0),
+    ("indexer slot from the row, not the position", "int64_t block_offset = pos % block_size;",
+     "int64_t block_offset = tid % block_size;", 0),
     ("task end not clamped to num_tokens",
      "int64_t e = min64(request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal), num_tokens);",
      "int64_t e = request_end(cu_seq_lens, r, num_reqs, num_tokens, terminal);", 1),

@@ -394,5 +394,146 @@ NAMED = {
 }
 
 
-def named(name: str) -> Workload:
+def named(name: str):
+    if name in INDEXER_NAMED:
+        return INDEXER_NAMED[name]()
     return NAMED[name]()
+
+
+# ---------------------------------------------------------------------------
+# indexer quant-cache gather (the per-row gather of page 3's
+# _cp_gather_indexer_quant_cache_kernel)
+# ---------------------------------------------------------------------------
+
+INDEXER_LAYOUT_FLAT = 0
+INDEXER_LAYOUT_TILED = 1
+INDEXER = "indexer"
+
+
+@dataclasses.dataclass
+class IndexerWorkload:
+    """Inputs of one indexer quant-cache gather.  The cache is [num_blocks,
+    block_stride] bytes of packed block records whose bytes are drawn uniformly
+    (the gather copies bytes, so no byte pattern is special); the generator
+    does not place values or scales, it only draws bytes."""
+    name: str
+    layout: int
+    head_dim: int
+    block_tile: int
+    head_tile: int
+    block_size: int
+    cache: torch.Tensor          # uint8 [num_blocks, block_stride]
+    token_to_seq: torch.Tensor   # int32 [num_tokens]
+    cu_seqlen: torch.Tensor      # int32 [num_batches + 1]
+    block_table: torch.Tensor    # int32 [num_batches, ld]; columns [0, block_table_width) are read
+    block_table_width: int
+    num_tokens: int
+    values: torch.Tensor         # uint8 [workspace_rows, value_cols], sentinel filled
+    scales: torch.Tensor         # float32 [workspace_rows, scale_cols], sentinel bytes
+    kind: str = INDEXER
+
+    @property
+    def num_blocks(self) -> int:
+        return self.cache.shape[0]
+
+    @property
+    def block_stride(self) -> int:
+        return self.cache.stride(0)
+
+    @property
+    def num_batches(self) -> int:
+        return self.cu_seqlen.numel() - 1
+
+    def to(self, device) -> "IndexerWorkload":
+        d = dataclasses.replace(self)
+        for f in ("cache", "token_to_seq", "cu_seqlen", "block_table", "values", "scales"):
+            setattr(d, f, getattr(self, f).to(device))
+        return d
+
+    def fresh_values(self) -> torch.Tensor:
+        return torch.full_like(self.values, SENTINEL_BYTE)
+
+    def fresh_scales(self) -> torch.Tensor:
+        return torch.full_like(self.scales.view(torch.uint8), SENTINEL_BYTE).view(torch.float32)
+
+    def dst_values(self, values=None) -> torch.Tensor:
+        v = self.values if values is None else values
+        return v[: self.num_tokens, : self.head_dim]
+
+    def dst_scales(self, scales=None) -> torch.Tensor:
+        s = self.scales if scales is None else scales
+        return s[: self.num_tokens, 0]
+
+    def gathered_rows(self) -> int:
+        """Rows whose batch id and extent are consistent (before block guards)."""
+        t2s = self.token_to_seq[: self.num_tokens].tolist()
+        cu = self.cu_seqlen.tolist()
+        B = self.num_batches
+        return sum(1 for t, b in enumerate(t2s) if 0 <= b < B and cu[b] <= t < cu[b + 1])
+
+    def algorithmic_bytes(self) -> int:
+        """Per row: head_dim value bytes and a 4-byte scale read and written, and
+        its 4-byte token_to_seq entry; plus cu_seqlen once per batch."""
+        rows = self.gathered_rows()
+        return rows * 2 * (self.head_dim + 4) + 4 * self.num_tokens + 4 * (self.num_batches + 1)
+
+
+def make_indexer_workload(name: str, seq_lens, block_size: int, head_dim: int, num_blocks: int,
+                          seed: int, *, layout: int = INDEXER_LAYOUT_FLAT, block_tile: int = 16,
+                          head_tile: int = 16, record_pad: int = 0, pad_rows: int = 0,
+                          value_cols: Optional[int] = None, scale_cols: int = 1,
+                          width: Optional[int] = None, allow_alias: bool = False) -> IndexerWorkload:
+    """Sequences of ``seq_lens`` tokens gathered into rows cu_seqlen[b] ..
+    cu_seqlen[b + 1]; token_to_seq names each row's sequence and is -1 for the
+    ``pad_rows`` rows after the last sequence (num_tokens = sum + pad_rows).
+    Block records are block_size * (head_dim + 4) + record_pad bytes.  Draw
+    order: block permutation, then cache bytes."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    seq_lens = [int(x) for x in seq_lens]
+    bt = deal_block_table(gen, seq_lens, block_size, num_blocks, width, allow_alias)
+    stride = block_size * (head_dim + 4) + record_pad
+    cache = torch.randint(0, 256, (num_blocks, stride), generator=gen, dtype=torch.uint8)
+    cu = prefix_sums(seq_lens)
+    total = int(cu[-1])
+    T = total + pad_rows
+    t2s = torch.full((T,), -1, dtype=torch.int32)
+    for b, n in enumerate(seq_lens):
+        t2s[int(cu[b]): int(cu[b]) + n] = b
+    value_cols = head_dim if value_cols is None else value_cols
+    values = torch.full((T, value_cols), SENTINEL_BYTE, dtype=torch.uint8)
+    scales = torch.full((T, 4 * scale_cols), SENTINEL_BYTE, dtype=torch.uint8).view(torch.float32)
+    return IndexerWorkload(name=name, layout=layout, head_dim=head_dim, block_tile=block_tile,
+                           head_tile=head_tile, block_size=block_size, cache=cache,
+                           token_to_seq=t2s, cu_seqlen=cu, block_table=bt,
+                           block_table_width=bt.shape[1], num_tokens=T, values=values,
+                           scales=scales)
+
+
+def indexer_single(tokens: int, layout: int, seed: int) -> IndexerWorkload:
+    """One sequence of `tokens` tokens, block 64, head_dim 128 fp8 values plus one
+    fp32 scale per token, 5/4 of the blocks needed, shuffled."""
+    tag = "tiled" if layout == INDEXER_LAYOUT_TILED else "flat"
+    pages = -(-tokens // 64)
+    return make_indexer_workload(f"indexer_single_{tokens // 1024}k_{tag}", [tokens], 64, 128,
+                                 pages * 5 // 4, seed, layout=layout)
+
+
+def indexer_skew8(layout: int, seed: int) -> IndexerWorkload:
+    """The skew-8 lengths as indexer sequences (block 64, head_dim 128), 3000
+    shuffled blocks, 8 padding rows (token_to_seq -1) after the last sequence."""
+    tag = "tiled" if layout == INDEXER_LAYOUT_TILED else "flat"
+    return make_indexer_workload(f"indexer_skew8_{tag}", SKEW8_LENS, 64, 128, 3000, seed,
+                                 layout=layout, pad_rows=8)
+
+
+INDEXER_NAMED = {
+    "indexer_tiny_flat": lambda: make_indexer_workload("indexer_tiny_flat", [17, 71, 0], 16, 128,
+                                                        32, 1501, pad_rows=5),
+    "indexer_tiny_tiled": lambda: make_indexer_workload("indexer_tiny_tiled", [17, 71, 0], 16, 128,
+                                                         32, 1502, layout=INDEXER_LAYOUT_TILED,
+                                                         pad_rows=5),
+    "indexer_single_300k_flat": lambda: indexer_single(307200, INDEXER_LAYOUT_FLAT, 1503),
+    "indexer_single_300k_tiled": lambda: indexer_single(307200, INDEXER_LAYOUT_TILED, 1504),
+    "indexer_skew8_flat": lambda: indexer_skew8(INDEXER_LAYOUT_FLAT, 1505),
+    "indexer_skew8_tiled": lambda: indexer_skew8(INDEXER_LAYOUT_TILED, 1506),
+}
