@@ -40,6 +40,7 @@ DEFAULT_WORKLOAD = "single_300k_fp8_upconvert"
 SECOND_WORKLOAD = "single_60k_raw"
 TRAFFIC_DIR = os.path.join(REPO, "profiles")
 KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp",
+                  "paged_kv_cache_device_amd/csrc/indexer_kernels.hpp",
                   "paged_kv_cache_device_amd/csrc/pkvg_capi.hip"]
 
 

@@ -10,7 +10,10 @@
  * workgroup per logical page, partial first/last pages, vector and scalar
  * stride paths; step 2: the destination is sliced to exactly num_tokens rows)
  * and "key source snippets" (the page-task fields and the per-token
- * reference the kernels must match).
+ * reference the kernels must match).  gather_indexer_quant_cache is the
+ * per-row indexer gather of the summary of pull request 56153 and keeps its
+ * own argument conventions, given with its declaration; the conventions below
+ * are those of the paged gathers.
  *
  * Conventions shared by every entry point
  * ----------------------------------------
@@ -73,7 +76,7 @@ extern "C" {
 #define PKVG_E_SHAPE 2  /* a count or size is out of range (negative, zero where positive is required) */
 #define PKVG_E_STRIDE 3 /* a stride is negative, or the destination rows overlap (dst_row_stride < entry),
                            or block_table_ld < block_table_width */
-#define PKVG_E_DTYPE 4  /* unsupported element size or kv_cache_dtype */
+#define PKVG_E_DTYPE 4  /* unsupported element size, kv_cache_dtype or indexer record layout */
 #define PKVG_E_LIMIT 5  /* beyond an implementation limit: num_tokens >= 2^31; one page's rows
                            span >= 2^31 bytes (block_size * row bytes, or (block_size - 1) *
                            token stride + row bytes); or num_tokens / block_size + 2 * num_reqs
@@ -198,6 +201,71 @@ int gather_page_tasks(const int32_t *cu_seq_lens, int32_t cu_terminal, const int
                       int64_t block_table_ld, int64_t num_blocks,
                       int32_t *tasks, int64_t capacity, int32_t *num_tasks,
                       void *stream);
+
+/*
+ * gather_indexer_quant_cache -- the indexer quant-cache gather: the per-row
+ * kernel of the prhub.com.cn summary of vLLM pull request 56153, "indexer
+ * kernel takes runtime arguments; no per-shape recompiles" (section "key
+ * source snippets": the masks and the clamp-then-widen block addressing;
+ * section "implementation breakdown", steps 2-4: layout, head dimension and
+ * tile sizes are structural, every shape-derived value is a runtime argument).
+ *
+ * Output row tid (0 <= tid < num_tokens) belongs to batch
+ * b = token_to_seq[tid]; it is written only if 0 <= b < num_batches,
+ * cu_seqlen[b] <= tid < cu_seqlen[b + 1], the block-table column
+ * pos / block_size (pos = tid - cu_seqlen[b]) is below block_table_width, and
+ * the physical block block_table[b * block_table_ld + column] lies in
+ * [0, num_blocks).  Any other row is left untouched (padding rows carry -1).
+ * A written row receives slot pos % block_size of that block: its head_dim
+ * value bytes into dst_values[tid][0 .. head_dim) and its 4-byte fp32 scale
+ * into dst_scales[tid * dst_scale_stride], both copied bit for bit.
+ *
+ * The cache is [num_blocks] packed block records of block_stride bytes (the
+ * page elides the record; the reading taken): the values of the block's
+ * block_size tokens first, head_dim bytes per token, then one fp32 scale per
+ * token in token order at byte block_size * head_dim.  The value bytes are
+ *   PKVG_INDEXER_FLAT:  token o, byte d at o * head_dim + d;
+ *   PKVG_INDEXER_TILED: in block_tile x head_tile tiles stored tile after
+ *     tile, tile rows outermost: at ((o / bt) * (head_dim / ht) + d / ht) *
+ *     bt * ht + (o % bt) * ht + d % ht.
+ *
+ *   cache             device, dword-aligned; block_stride bytes per record,
+ *                     a multiple of 4, >= block_size * (head_dim + 4), < 2^31
+ *   num_blocks        >= 0 (the block-id bound); block_size > 0
+ *   layout, head_dim, block_tile, head_tile
+ *                     structural: FLAT with head_dim 64, 128 or 256 (tiles
+ *                     ignored), or TILED with head_dim 64, 128 or 256 and
+ *                     16 x 16 tiles (block_size a multiple of 16); else
+ *                     PKVG_E_DTYPE
+ *   dst_values        device bytes [num_tokens, >= head_dim], row stride
+ *                     dst_value_stride bytes (>= head_dim)
+ *   dst_scales        device fp32 [num_tokens], stride dst_scale_stride
+ *                     elements (>= 1), dword-aligned
+ *   num_tokens        >= 0, <= 2^31 - 65
+ *   token_to_seq      device int32 [num_tokens]
+ *   cu_seqlen         device int32 [num_batches + 1] (entries past it are never read)
+ *   block_table       device int32 rows of pitch block_table_ld >= block_table_width;
+ *                     may be NULL when block_table_width == 0
+ *   stream            hipStream_t or NULL
+ *
+ * Nothing is allocated; one kernel is enqueued.  num_tokens == 0 or
+ * num_batches == 0 returns PKVG_OK without enqueueing anything.  Errors
+ * (before anything is enqueued): PKVG_E_NULL, PKVG_E_SHAPE, PKVG_E_STRIDE
+ * (also a misaligned cache, record stride or dst_scales), PKVG_E_DTYPE,
+ * PKVG_E_LIMIT, PKVG_E_HIP.
+ */
+#define PKVG_INDEXER_FLAT 0
+#define PKVG_INDEXER_TILED 1
+
+int gather_indexer_quant_cache(const void *cache, int64_t num_blocks, int32_t block_size,
+                               int64_t block_stride, int32_t layout, int32_t head_dim,
+                               int32_t block_tile, int32_t head_tile,
+                               void *dst_values, int64_t dst_value_stride,
+                               float *dst_scales, int64_t dst_scale_stride,
+                               int64_t num_tokens, const int32_t *token_to_seq,
+                               const int32_t *cu_seqlen, int32_t num_batches,
+                               const int32_t *block_table, int32_t block_table_width,
+                               int64_t block_table_ld, void *stream);
 
 /*
  * pkvg_plan -- how a gather call with these arguments would run, worked out

@@ -18,6 +18,9 @@ Entry points (names as in the C ABI):
   block_table, num_blocks, capacity=None)``
 * ``pkvg_plan(op, kind, ...)``: how a call would run (kernel, shape, task units,
   grid), from plain sizes, strides and addresses; nothing is enqueued
+* ``gather_indexer_quant_cache(cache, dst_values, dst_scales, token_to_seq,
+  cu_seqlen, block_table, block_size, layout='flat', ...)``: the indexer
+  quant-cache gather (per output row, keyed by ``token_to_seq``)
 
 ``src_cache`` is a [num_blocks, block_size, entry] view (innermost stride 1;
 a view of wider rows is fine), ``dst`` a [num_tokens, entry] view (innermost
@@ -56,6 +59,8 @@ PKVG_TASKS_WAVE = 0
 PKVG_TASKS_LDS = 1
 PKVG_TASKS_TABLE = 2
 PKVG_TASKS_SINGLE = 3
+PKVG_INDEXER_FLAT = 0
+PKVG_INDEXER_TILED = 1
 
 # the C entry points and their argument types, as declared in include/pkvg.h
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -67,6 +72,8 @@ SIGNATURES = {
     "gather_page_tasks": [_vp, _i32, _vp, _i32, _i64, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp,
                           _vp],
     "pkvg_plan": [_i32, _i32, _vp] + _CACHE_ARGS + [_vp, _vp],
+    "gather_indexer_quant_cache": [_vp, _i64, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _i64, _vp,
+                                   _i64, _i64, _vp, _vp, _i32, _vp, _i32, _i64, _vp],
     "pkvg_status_string": [ctypes.c_int],
     "pkvg_last_hip_error": [],
 }
@@ -354,3 +361,57 @@ def pkvg_plan(op: int, kind: int, src: int, num_blocks: int, block_size: int, en
                                block_table_width, block_table_ld, cu_seq_lens, cu_terminal,
                                seq_starts, num_reqs, scale, ctypes.byref(info)), "pkvg_plan")
     return info.as_dict()
+
+
+_INDEXER_LAYOUTS = {"flat": PKVG_INDEXER_FLAT, "tiled": PKVG_INDEXER_TILED}
+
+
+def prepare_indexer(cache: torch.Tensor, dst_values: torch.Tensor, dst_scales: torch.Tensor,
+                    token_to_seq: torch.Tensor, cu_seqlen: torch.Tensor, block_table: torch.Tensor,
+                    block_size: int, layout: str = "flat", *, block_tile: int = 16,
+                    head_tile: int = 16, num_batches: int | None = None,
+                    block_table_width: int | None = None) -> PreparedCall:
+    """Marshal one ``gather_indexer_quant_cache`` call on the current stream.
+
+    ``cache``: uint8 [num_blocks, block_stride] (unit inner stride) of packed
+    block records; ``dst_values``: uint8 [num_tokens, head_dim] view (unit
+    inner stride; head_dim is its column count); ``dst_scales``: float32
+    [num_tokens] (any positive stride); ``token_to_seq``: int32 [num_tokens];
+    ``cu_seqlen``: int32 [num_batches + 1]; ``block_table``: int32
+    [num_batches, >= width]."""
+    if cache.dtype != torch.uint8 or cache.dim() != 2 or cache.stride(1) != 1 or not cache.is_cuda:
+        raise ValueError("cache must be a uint8 [num_blocks, block_stride] device tensor")
+    if (dst_values.dtype != torch.uint8 or dst_values.dim() != 2 or dst_values.stride(1) != 1
+            or not dst_values.is_cuda):
+        raise ValueError("dst_values must be a uint8 [num_tokens, head_dim] device view")
+    if dst_scales.dtype != torch.float32 or dst_scales.dim() != 1 or not dst_scales.is_cuda:
+        raise ValueError("dst_scales must be a float32 [num_tokens] device tensor")
+    _device_i32(token_to_seq, "token_to_seq", 1)
+    _device_i32(cu_seqlen, "cu_seqlen", 1)
+    _device_i32(block_table, "block_table", 2)
+    T = dst_values.shape[0]
+    if dst_scales.shape[0] != T or token_to_seq.numel() < T:
+        raise ValueError("dst_scales and token_to_seq need num_tokens entries")
+    nb = cu_seqlen.numel() - 1 if num_batches is None else num_batches
+    if cu_seqlen.numel() < nb + 1 or block_table.shape[0] < nb:
+        raise ValueError("cu_seqlen needs num_batches + 1 entries and block_table num_batches rows")
+    if layout not in _INDEXER_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_INDEXER_LAYOUTS)}")
+    width = block_table.shape[1] if block_table_width is None else block_table_width
+    _same_device([("cache", cache), ("dst_values", dst_values), ("dst_scales", dst_scales),
+                  ("token_to_seq", token_to_seq), ("cu_seqlen", cu_seqlen),
+                  ("block_table", block_table)])
+    return PreparedCall("gather_indexer_quant_cache", [
+        _ptr(cache), cache.shape[0], block_size, cache.stride(0), _INDEXER_LAYOUTS[layout],
+        dst_values.shape[1], block_tile, head_tile, _ptr(dst_values), dst_values.stride(0),
+        _ptr(dst_scales), dst_scales.stride(0), T, _ptr(token_to_seq), _ptr(cu_seqlen), nb,
+        _ptr(block_table), width, block_table.stride(0), _stream_handle()])
+
+
+def gather_indexer_quant_cache(cache, dst_values, dst_scales, token_to_seq, cu_seqlen, block_table,
+                               block_size: int, layout: str = "flat", **kwargs) -> None:
+    """Indexer quant-cache gather: rows of ``dst_values`` / ``dst_scales`` whose
+    batch, extent, table column and block are valid take their token's value
+    bytes and fp32 scale from the packed cache; other rows are untouched."""
+    prepare_indexer(cache, dst_values, dst_scales, token_to_seq, cu_seqlen, block_table,
+                    block_size, layout, **kwargs)()

@@ -9,6 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 REPO = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "pkvg_capi.hip")]
 DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "gather_kernels.hpp"),
+                     os.path.join(PKG, "csrc", "indexer_kernels.hpp"),
                      os.path.join(REPO, "include", "pkvg.h")]
 LIBRARY = os.path.join(PKG, "libpkvg.so")
 ARCH = "gfx950"

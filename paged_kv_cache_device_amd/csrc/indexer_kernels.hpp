@@ -1,0 +1,169 @@
+// indexer_kernels.hpp -- HIP device code of the indexer quant-cache gather for
+// gfx950 (CDNA4, wave64).
+//
+// Method: the prhub.com.cn summary of vLLM pull request 56153, "indexer kernel
+// takes runtime arguments; no per-shape recompiles", section "key source
+// snippets": each output row tid belongs to the batch token_to_seq[tid], whose
+// rows are [cu_seqlen[b], cu_seqlen[b + 1]); the row's position in its
+// sequence picks a block-table column and an in-block slot; masks on the batch
+// id, the row range, the column, the slot and the physical block id leave a
+// row untouched when any fails; the block id is clamped before it is widened
+// to 64 bits for the packed record's large stride.  Section "implementation
+// breakdown", steps 2-4: the record layout, the head dimension and the tile
+// sizes are structural (template parameters here); the token count, batch
+// count, table width and block count are runtime values used only in the
+// masks.
+//
+// The packed block record (the page elides it; the reading taken): the
+// block's block_size tokens' value bytes (HEAD_DIM each) first, token-major
+// (flat) or in BT x HT tiles stored tile after tile, tile rows outermost; then
+// one 4-byte fp32 scale per token, in token order, at byte block_size *
+// HEAD_DIM of the record.
+//
+// Design for gfx950: the work unit is the output row (token_to_seq may send
+// any row to any batch, and padding rows carry -1), so a wave owns 64
+// consecutive rows.  Lane r resolves row r (token_to_seq, the batch's extent,
+// the block-table entry: three dependent loads) to a source address; then
+// the wave moves the 64 rows' value bytes in W-byte chunks, consecutive lanes
+// on consecutive chunks of consecutive rows (a 16-byte chunk per lane puts
+// 1 KiB of contiguous rows under one wave instruction), taking each row's
+// address from its owner lane with a cross-lane read; each lane then moves its
+// own row's 4-byte scale.  Loads of all of a lane's chunks go out before its
+// stores, with the nontemporal policy (each byte is touched once).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkvg {
+
+enum IndexerLayout : int {
+  kIndexerFlat = 0,   // token o, byte d of the value area at o * HEAD_DIM + d
+  kIndexerTiled = 1,  // BT x HT tiles, tile rows outermost, token-major inside a tile
+};
+
+struct IndexerParams {
+  const uint8_t* cache;           // record 0, byte 0
+  uint8_t* dst_values;            // row 0, byte 0
+  uint8_t* dst_scales;            // row 0's fp32 scale
+  const int32_t* token_to_seq;    // [num_tokens]
+  const int32_t* cu_seqlen;       // [num_batches + 1]
+  const int32_t* block_table;     // [num_batches, ld]; NULL when block_table_width == 0
+  int64_t block_stride;           // bytes per record
+  int64_t dst_value_stride;       // bytes
+  int64_t dst_scale_stride;       // bytes
+  int64_t block_table_ld;         // int32 elements
+  int64_t num_blocks;
+  int32_t num_tokens;
+  int32_t num_batches;
+  int32_t block_table_width;
+  int32_t block_size;
+  uint32_t block_size_magic;      // ceil(2^32 / block_size), or 0xFFFFFFFF for 1
+  uint32_t scale_area;            // block_size * HEAD_DIM: byte of the first scale in a record
+};
+
+constexpr int kIndexerThreads = 256;
+constexpr int kIndexerRowsPerWave = 64;
+
+// Byte offset, inside a record's value area, of chunk j (bytes j*W .. j*W+W-1)
+// of a token whose row starts at `row_base` (flat: slot * HEAD_DIM; tiled: the
+// tile row's start plus the slot's row inside its tile).  A chunk never
+// crosses a tile (W divides HT).
+template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W>
+__device__ __forceinline__ uint32_t indexer_chunk_offset(uint32_t row_base, uint32_t j) {
+  const uint32_t d = j * W;
+  if constexpr (LAYOUT == kIndexerFlat) {
+    return row_base + d;
+  } else {
+    static_assert(HT % W == 0, "a chunk stays inside one tile");
+    return row_base + (d / HT) * (BT * HT) + d % HT;
+  }
+}
+
+template <int LAYOUT, int HEAD_DIM, int BT, int HT>
+__device__ __forceinline__ uint32_t indexer_row_base(uint32_t slot) {
+  if constexpr (LAYOUT == kIndexerFlat) return slot * HEAD_DIM;
+  else return (slot / BT) * (HEAD_DIM * BT) + (slot % BT) * HT;
+}
+
+template <int W> struct IndexerChunk;
+template <> struct IndexerChunk<16> { using T = u32x4; };
+template <> struct IndexerChunk<1> { using T = uint8_t; };
+
+// Grid: any size; wave w of workgroup g takes rows from (g * 4 + w) * 64 on,
+// striding by the grid's rows.  Source rows are dword-aligned (the host checks
+// the cache base and the record stride; value rows start at multiples of 16
+// bytes inside a record), so bit 0 of a row's address carries its mask when
+// the address crosses lanes.
+template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W>
+__global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(IndexerParams p) {
+  using V = typename IndexerChunk<W>::T;
+  constexpr int CPR = HEAD_DIM / W;  // chunks per row
+  constexpr int WAVES = kIndexerThreads / 64;
+  static_assert(HEAD_DIM % W == 0 && HEAD_DIM % 16 == 0, "rows are whole chunks, 16-byte multiples");
+  // the wave's 64 rows are 64 * CPR chunks: CPR per lane, moved in batches of
+  // at most 16 loads in flight per lane (all of them for 16-byte chunks of
+  // rows up to 256 bytes)
+  constexpr int PER_LANE = CPR;
+  constexpr int BATCH = PER_LANE < 16 ? PER_LANE : 16;
+  static_assert(PER_LANE % BATCH == 0, "whole batches");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t stride_rows = int64_t(gridDim.x) * WAVES * kIndexerRowsPerWave;
+
+  for (int64_t row0 = (int64_t(blockIdx.x) * WAVES + wave) * kIndexerRowsPerWave; row0 < p.num_tokens;
+       row0 += stride_rows) {
+    // --- this lane's row: its batch, position, block and source ------------
+    const int32_t row = static_cast<int32_t>(row0) + lane;
+    bool ok = row < p.num_tokens;
+    const int32_t batch = p.token_to_seq[ok ? row : p.num_tokens - 1];
+    ok = ok && batch >= 0 && batch < p.num_batches;
+    const int32_t b = ok ? batch : 0;
+    const int32_t start = p.cu_seqlen[b];
+    const int32_t end = p.cu_seqlen[b + 1];
+    ok = ok && row >= start && row < end;
+    const uint32_t pos = ok ? static_cast<uint32_t>(row - start) : 0u;
+    const uint32_t col = div_magic(pos, static_cast<uint32_t>(p.block_size), p.block_size_magic);
+    const uint32_t slot = pos - col * static_cast<uint32_t>(p.block_size);
+    ok = ok && col < static_cast<uint32_t>(p.block_table_width);
+    int32_t block = -1;
+    if (ok) block = p.block_table[int64_t(b) * p.block_table_ld + col];
+    ok = ok && block >= 0 && block < p.num_blocks;
+    // clamped to block 0 when invalid, then widened: the record stride is large
+    const int64_t record = int64_t(ok ? block : 0) * p.block_stride;
+    const uint64_t src_bits =
+        reinterpret_cast<uint64_t>(p.cache + record + indexer_row_base<LAYOUT, HEAD_DIM, BT, HT>(slot));
+    const uint32_t src_lo = static_cast<uint32_t>(src_bits) | (ok ? 1u : 0u);
+    const uint32_t src_hi = static_cast<uint32_t>(src_bits >> 32);
+
+    // --- value bytes: chunk c = lane + 64k is chunk c % CPR of row c / CPR ---
+#pragma unroll
+    for (int k0 = 0; k0 < PER_LANE; k0 += BATCH) {
+      V v[BATCH];
+      bool take[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
+        const int r = static_cast<int>(c / CPR);
+        const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(src_lo), r, 64));
+        const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(src_hi), r, 64));
+        take[k] = (lo & 1u) != 0u;
+        const uint8_t* q = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | (lo & ~1u));
+        if (take[k]) v[k] = load_stream<V>(q + indexer_chunk_offset<LAYOUT, HEAD_DIM, BT, HT, W>(0u, c % CPR));
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) {
+        const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
+        const int64_t r = row0 + static_cast<int64_t>(c / CPR);
+        if (take[k]) store_stream(p.dst_values + r * p.dst_value_stride + (c % CPR) * W, v[k]);
+      }
+    }
+    // --- the scale of this lane's own row ------------------------------------
+    if (ok) {
+      const uint32_t scale = load_stream<uint32_t>(p.cache + record + p.scale_area + slot * 4u);
+      store_stream(p.dst_scales + int64_t(row) * p.dst_scale_stride, scale);
+    }
+  }
+}
+
+}  // namespace pkvg

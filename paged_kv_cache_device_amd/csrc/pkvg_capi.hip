@@ -6,6 +6,7 @@
 // device; launches go to the caller's stream.
 #include "pkvg.h"
 #include "gather_kernels.hpp"
+#include "indexer_kernels.hpp"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,6 +17,8 @@ using pkvg::GatherParams;
 using pkvg::TaskRecord;
 
 static_assert(pkvg::kFusedMaxReqs == PKVG_FUSED_MAX_REQS, "the fused task paths cover the header's batch limit");
+static_assert(pkvg::kIndexerFlat == PKVG_INDEXER_FLAT && pkvg::kIndexerTiled == PKVG_INDEXER_TILED,
+              "the header's indexer layout codes are the kernel's");
 static_assert(pkvg::kWaveRegs == PKVG_TASKS_WAVE && pkvg::kLdsPrefix == PKVG_TASKS_LDS &&
                   pkvg::kTable == PKVG_TASKS_TABLE && pkvg::kSingle == PKVG_TASKS_SINGLE,
               "the header's task-mode codes are the kernel's");
@@ -508,9 +511,124 @@ int32_t shape_lane_bytes(int shape) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// indexer quant-cache gather
+// ---------------------------------------------------------------------------
+
+// Structural constants (template parameters): the record layout, the head
+// dimension and the tile sizes; every other size is a runtime argument.
+bool indexer_structure_supported(int32_t layout, int32_t head_dim, int32_t block_tile, int32_t head_tile) {
+  const bool dim = head_dim == 64 || head_dim == 128 || head_dim == 256;
+  if (layout == PKVG_INDEXER_FLAT) return dim;
+  if (layout == PKVG_INDEXER_TILED) return dim && block_tile == 16 && head_tile == 16;
+  return false;
+}
+
+template <int LAYOUT, int HEAD_DIM, int BT, int HT>
+hipError_t launch_indexer_w(const pkvg::IndexerParams& p, bool vec, unsigned grid, hipStream_t stream) {
+  if (vec)
+    return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, 16>, grid, pkvg::kIndexerThreads, 0,
+                  stream, p);
+  return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, 1>, grid, pkvg::kIndexerThreads, 0,
+                stream, p);
+}
+
+template <int LAYOUT, int BT, int HT>
+hipError_t launch_indexer_dim(const pkvg::IndexerParams& p, int32_t head_dim, bool vec, unsigned grid,
+                              hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_indexer_w<LAYOUT, 64, BT, HT>(p, vec, grid, stream);
+    case 128: return launch_indexer_w<LAYOUT, 128, BT, HT>(p, vec, grid, stream);
+    default: return launch_indexer_w<LAYOUT, 256, BT, HT>(p, vec, grid, stream);
+  }
+}
+
+// Rows per workgroup (four waves of 64 rows); the grid covers every row once,
+// up to this many workgroups (more rows are taken by striding).
+constexpr int64_t kIndexerMaxGrid = int64_t(1) << 20;
+
+// Validates an indexer gather and fills its parameters; touches no device.
+int prepare_indexer(const void* cache, int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                    int32_t layout, int32_t head_dim, int32_t block_tile, int32_t head_tile, void* dst_values,
+                    int64_t dst_value_stride, float* dst_scales, int64_t dst_scale_stride, int64_t num_tokens,
+                    const int32_t* token_to_seq, const int32_t* cu_seqlen, int32_t num_batches,
+                    const int32_t* block_table, int32_t block_table_width, int64_t block_table_ld,
+                    pkvg::IndexerParams* out, bool* vec, bool* nothing) {
+  *nothing = false;
+  if (num_tokens < 0 || num_batches < 0 || num_blocks < 0 || block_table_width < 0 || block_size <= 0)
+    return PKVG_E_SHAPE;
+  if (!indexer_structure_supported(layout, head_dim, block_tile, head_tile)) return PKVG_E_DTYPE;
+  if (layout == PKVG_INDEXER_TILED && block_size % block_tile != 0) return PKVG_E_SHAPE;
+  const int64_t record_bytes = int64_t(block_size) * (head_dim + 4);
+  if (block_stride < record_bytes || dst_value_stride < head_dim || dst_scale_stride < 1 ||
+      block_table_ld < block_table_width)
+    return PKVG_E_STRIDE;
+  if (num_tokens == 0 || num_batches == 0) {
+    *nothing = true;
+    return PKVG_OK;
+  }
+  if (!cache || !dst_values || !dst_scales || !token_to_seq || !cu_seqlen ||
+      (!block_table && block_table_width > 0))
+    return PKVG_E_NULL;
+  // the records hold fp32 scales: dword-aligned records; fp32 destination scales
+  if (!aligned(cache, 4) || block_stride % 4 != 0 || !aligned(dst_scales, 4)) return PKVG_E_STRIDE;
+  // rows are int32 (a wave's 64 rows stay below 2^31); in-record offsets are 32-bit
+  if (num_tokens > INT32_MAX - 64 || block_stride >= (int64_t(1) << 31)) return PKVG_E_LIMIT;
+  if (dst_scale_stride > INT64_MAX / 4) return PKVG_E_LIMIT;
+  pkvg::IndexerParams& p = *out;
+  p = pkvg::IndexerParams{};
+  p.cache = static_cast<const uint8_t*>(cache);
+  p.dst_values = static_cast<uint8_t*>(dst_values);
+  p.dst_scales = reinterpret_cast<uint8_t*>(dst_scales);
+  p.token_to_seq = token_to_seq;
+  p.cu_seqlen = cu_seqlen;
+  p.block_table = block_table;
+  p.block_stride = block_stride;
+  p.dst_value_stride = dst_value_stride;
+  p.dst_scale_stride = dst_scale_stride * 4;
+  p.block_table_ld = block_table_ld;
+  p.num_blocks = num_blocks;
+  p.num_tokens = static_cast<int32_t>(num_tokens);
+  p.num_batches = num_batches;
+  p.block_table_width = block_table_width;
+  p.block_size = block_size;
+  p.block_size_magic = magic_for(static_cast<uint32_t>(block_size));
+  p.scale_area = static_cast<uint32_t>(int64_t(block_size) * head_dim);
+  // 16-byte chunks need dword-aligned destination rows (the source rows are)
+  *vec = aligned(dst_values, 4) && dst_value_stride % 4 == 0;
+  return PKVG_OK;
+}
+
+int64_t indexer_grid(int64_t num_tokens) {
+  const int64_t rows_per_wg = int64_t(pkvg::kIndexerThreads / 64) * pkvg::kIndexerRowsPerWave;
+  const int64_t g = (num_tokens + rows_per_wg - 1) / rows_per_wg;
+  return g < kIndexerMaxGrid ? g : kIndexerMaxGrid;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gather_indexer_quant_cache(const void* cache, int64_t num_blocks, int32_t block_size, int64_t block_stride,
+                               int32_t layout, int32_t head_dim, int32_t block_tile, int32_t head_tile,
+                               void* dst_values, int64_t dst_value_stride, float* dst_scales,
+                               int64_t dst_scale_stride, int64_t num_tokens, const int32_t* token_to_seq,
+                               const int32_t* cu_seqlen, int32_t num_batches, const int32_t* block_table,
+                               int32_t block_table_width, int64_t block_table_ld, void* stream) {
+  pkvg::IndexerParams p;
+  bool vec = false, nothing = false;
+  const int st = prepare_indexer(cache, num_blocks, block_size, block_stride, layout, head_dim, block_tile,
+                                 head_tile, dst_values, dst_value_stride, dst_scales, dst_scale_stride, num_tokens,
+                                 token_to_seq, cu_seqlen, num_batches, block_table, block_table_width,
+                                 block_table_ld, &p, &vec, &nothing);
+  if (st != PKVG_OK || nothing) return st;
+  const unsigned grid = static_cast<unsigned>(indexer_grid(num_tokens));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = layout == PKVG_INDEXER_FLAT
+                           ? launch_indexer_dim<pkvg::kIndexerFlat, 1, 16>(p, head_dim, vec, grid, s)
+                           : launch_indexer_dim<pkvg::kIndexerTiled, 16, 16>(p, head_dim, vec, grid, s);
+  return e == hipSuccess ? PKVG_OK : hip_fail(e);
+}
 
 int gather_cache(const void* src_cache, int32_t elem_bytes, int64_t num_blocks, int32_t block_size,
                  int32_t entry, int64_t src_block_stride, int64_t src_token_stride, void* dst,
@@ -620,7 +738,7 @@ const char* pkvg_status_string(int status) {
     case PKVG_E_NULL: return "PKVG_E_NULL: a required pointer is NULL";
     case PKVG_E_SHAPE: return "PKVG_E_SHAPE: a count or size is out of range";
     case PKVG_E_STRIDE: return "PKVG_E_STRIDE: a stride is negative or rows overlap";
-    case PKVG_E_DTYPE: return "PKVG_E_DTYPE: unsupported element size or kv_cache_dtype";
+    case PKVG_E_DTYPE: return "PKVG_E_DTYPE: unsupported element size, kv_cache_dtype or record layout";
     case PKVG_E_LIMIT: return "PKVG_E_LIMIT: beyond an implementation limit";
     case PKVG_E_HIP: return "PKVG_E_HIP: a HIP runtime call failed";
     default: return "unknown pkvg status";

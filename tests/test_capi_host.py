@@ -132,3 +132,46 @@ def test_binding_rejects_host_tensors():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         pkvg.library(str(tmp_path / "missing.so"))
+
+
+def _ix(lib, **kw):
+    a = dict(cache=FAKE, nb=4, bs=16, bstride=16 * 132, layout=pkvg.PKVG_INDEXER_FLAT, hd=128,
+             bt_=16, ht=16, vals=FAKE, vstride=128, scales=FAKE, sstride=1, T=10, t2s=FAKE, cu=FAKE,
+             B=2, table=FAKE, W=3, ld=3)
+    a.update(kw)
+    return lib.gather_indexer_quant_cache(
+        a["cache"], a["nb"], a["bs"], a["bstride"], a["layout"], a["hd"], a["bt_"], a["ht"], a["vals"],
+        a["vstride"], a["scales"], a["sstride"], a["T"], a["t2s"], a["cu"], a["B"], a["table"],
+        a["W"], a["ld"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layout=2), pkvg.PKVG_E_DTYPE),                       # unknown record layout
+    (dict(hd=96), pkvg.PKVG_E_DTYPE),                          # head_dim not built
+    (dict(layout=pkvg.PKVG_INDEXER_TILED, bt_=8), pkvg.PKVG_E_DTYPE),   # tile shape not built
+    (dict(layout=pkvg.PKVG_INDEXER_TILED, bs=8, bstride=8 * 132), pkvg.PKVG_E_SHAPE),  # bs % 16
+    (dict(bs=0), pkvg.PKVG_E_SHAPE),
+    (dict(T=-1), pkvg.PKVG_E_SHAPE),
+    (dict(B=-1), pkvg.PKVG_E_SHAPE),
+    (dict(nb=-1), pkvg.PKVG_E_SHAPE),
+    (dict(W=-1), pkvg.PKVG_E_SHAPE),
+    (dict(bstride=16 * 132 - 4), pkvg.PKVG_E_STRIDE),         # record shorter than values + scales
+    (dict(vstride=127), pkvg.PKVG_E_STRIDE),
+    (dict(sstride=0), pkvg.PKVG_E_STRIDE),
+    (dict(ld=2), pkvg.PKVG_E_STRIDE),
+    (dict(bstride=16 * 132 + 2), pkvg.PKVG_E_STRIDE),         # records not dword-aligned
+    (dict(cache=FAKE + 2), pkvg.PKVG_E_STRIDE),
+    (dict(scales=FAKE + 2), pkvg.PKVG_E_STRIDE),
+    (dict(cache=None), pkvg.PKVG_E_NULL),
+    (dict(vals=None), pkvg.PKVG_E_NULL),
+    (dict(scales=None), pkvg.PKVG_E_NULL),
+    (dict(t2s=None), pkvg.PKVG_E_NULL),
+    (dict(cu=None), pkvg.PKVG_E_NULL),
+    (dict(table=None), pkvg.PKVG_E_NULL),
+    (dict(T=1 << 31), pkvg.PKVG_E_LIMIT),
+    (dict(bstride=1 << 31), pkvg.PKVG_E_LIMIT),
+    (dict(T=0, cache=None, vals=None, scales=None, t2s=None, cu=None, table=None), pkvg.PKVG_OK),
+    (dict(B=0, cache=None, vals=None, scales=None, t2s=None, cu=None, table=None), pkvg.PKVG_OK),
+])
+def test_indexer_argument_checks(lib, kw, code):
+    assert _ix(lib, **kw) == code
