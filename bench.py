@@ -101,7 +101,7 @@ def summarize_counters(prof_dir: str, workload: str, calib_mib: int, command: st
     for kind, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
         rs = [r for r in rows(kind) if r["Counter_Name"] == counter]
         gather = [float(r["Counter_Value"]) for r in rs
-                  if "gather_pages_kernel" in r["Kernel_Name"] or "gather_groups_kernel" in r["Kernel_Name"]]
+                  if any(k in r["Kernel_Name"] for k in GATHER_KERNELS)]
         copies = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]][-10:]
         known = calib_mib << 20
         factor = known / (statistics.median(copies) * 1024.0)
@@ -120,11 +120,22 @@ def summarize_counters(prof_dir: str, workload: str, calib_mib: int, command: st
     return res
 
 
+INDEXER_LAYOUT_NAMES = {0: "flat", 1: "tiled"}
+# the library's data-moving kernels (the builder kernels of large batches are not counted)
+GATHER_KERNELS = ("gather_pages_kernel", "gather_groups_kernel", "indexer_gather_kernel")
+
+
 def call_for(wl, ws):
-    """The library call for workload ``wl`` into workspace ``ws``, marshalled once."""
+    """The library call for workload ``wl`` into workspace ``ws`` (for an
+    indexer workload: its own value and scale destinations), marshalled once."""
     import paged_kv_cache_device_amd as pkvg
     import workloads
 
+    if wl.kind == workloads.INDEXER:
+        return pkvg.prepare_indexer(wl.cache, wl.dst_values(), wl.dst_scales(), wl.token_to_seq,
+                                    wl.cu_seqlen, wl.block_table, wl.block_size,
+                                    INDEXER_LAYOUT_NAMES[wl.layout], block_tile=wl.block_tile,
+                                    head_tile=wl.head_tile, block_table_width=wl.block_table_width)
     dst = ws[: wl.num_tokens, : wl.entry]
     common = (wl.src_cache(), dst, wl.block_table, wl.cu_seq_lens, wl.num_reqs)
     if wl.kind == workloads.RAW:
@@ -138,19 +149,28 @@ def call_for(wl, ws):
     return pkvg.prepare("gather_maybe_dequant", *common, "auto", seq_starts=wl.seq_starts)
 
 
+def _bulk_fields(wl):
+    """The large tensors of a workload: the ones each rotation set copies."""
+    import workloads
+
+    if wl.kind == workloads.INDEXER:
+        return ("cache", "values", "scales")
+    return ("cache_base", "workspace")
+
+
 def make_sets(wl_dev, min_bytes: int):
-    """Copies of (cache, workspace) on the device totalling >= min_bytes."""
+    """Copies of a workload's cache and destinations on the device totalling >= min_bytes."""
     import dataclasses
 
-    per = wl_dev.cache_base.numel() * wl_dev.cache_base.element_size() + \
-        wl_dev.workspace.numel() * wl_dev.workspace.element_size()
+    fields = _bulk_fields(wl_dev)
+    per = sum(getattr(wl_dev, f).numel() * getattr(wl_dev, f).element_size() for f in fields)
     n = max(2, -(-min_bytes // per))
     sets = []
     for i in range(n):
         w = dataclasses.replace(wl_dev)
         if i:
-            w.cache_base = wl_dev.cache_base.clone()
-            w.workspace = wl_dev.workspace.clone()
+            for f in fields:
+                setattr(w, f, getattr(wl_dev, f).clone())
         sets.append(w)
     return sets
 
@@ -162,7 +182,7 @@ def time_steps(sets, steps: int, warmup: int):
     before the first and right after the last call."""
     import torch
 
-    runs = [call_for(w, w.workspace) for w in sets]
+    runs = [call_for(w, getattr(w, "workspace", None)) for w in sets]
     for i in range(warmup):
         runs[i % len(runs)]()
     torch.cuda.synchronize()
@@ -185,7 +205,7 @@ def cold_latency(wl_dev, reps: int, scrub_bytes: int = 1 << 30):
     import torch
 
     scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=wl_dev.workspace.device)
-    run = call_for(wl_dev, wl_dev.workspace)
+    run = call_for(wl_dev, getattr(wl_dev, "workspace", None))
     out = []
     for i in range(reps + 3):
         scrub.fill_(i)
@@ -250,6 +270,39 @@ def oracle_row_chunks(wl, parts: int):
     return chunks
 
 
+def indexer_oracle_threaded(wl, threads: int, values, scales):
+    """A callable that runs the oracle's indexer gather once over `threads`
+    disjoint row ranges [r0, r1) of `wl`: each range passes token_to_seq and
+    the destinations from row r0 on and cu_seqlen shifted down by r0, so row
+    r0 + i of the whole gather is row i of the range with the same position in
+    its sequence (the oracle's code and arithmetic are unchanged)."""
+    import numpy as np
+
+    import oracle
+
+    o = oracle.load()
+    T = wl.num_tokens
+    per = max(1, -(-T // threads))
+    cache = wl.cache.numpy().reshape(-1)
+    vflat = values.numpy().reshape(-1)
+    sflat = scales.view(__import__("torch").uint8).numpy().reshape(-1)
+    vs, ss = values.stride(0), 4 * scales.stride(0)
+    t2s = wl.token_to_seq.numpy()
+    cu = wl.cu_seqlen.numpy().astype(np.int64)
+    bt = wl.block_table.numpy()
+    jobs = [(r0, min(r0 + per, T)) for r0 in range(0, T, per)]
+
+    def run(job):
+        r0, r1 = job
+        return o.indexer_gather(cache, wl.num_blocks, wl.block_size, wl.block_stride, wl.layout,
+                                wl.head_dim, wl.block_tile, wl.head_tile, vflat[r0 * vs:], vs,
+                                sflat[r0 * ss:], ss, r1 - r0, t2s[r0:r1],
+                                (cu - r0).astype(np.int32), wl.num_batches, bt,
+                                wl.block_table_width, bt.shape[1])
+
+    return lambda pool: sum(pool.map(run, jobs))
+
+
 def oracle_threaded(wl, threads: int, ws):
     """A callable that runs the oracle once over `threads` disjoint row ranges of
     `wl` into the workspace `ws` (on a given thread pool) and returns the rows
@@ -283,7 +336,12 @@ def cpu_baseline(wl, seconds: float = 10.0, threads: int = 1):
     arithmetic are unchanged; ctypes releases the GIL during each call)."""
     from concurrent.futures import ThreadPoolExecutor
 
-    run_once = oracle_threaded(wl, threads, wl.fresh_workspace())
+    import workloads
+
+    if wl.kind == workloads.INDEXER:
+        run_once = indexer_oracle_threaded(wl, threads, wl.fresh_values(), wl.fresh_scales())
+    else:
+        run_once = oracle_threaded(wl, threads, wl.fresh_workspace())
     reps = 0
     with ThreadPoolExecutor(max_workers=threads) as pool:
         t0 = time.perf_counter()
@@ -348,13 +406,10 @@ def measure(wl, dev, args) -> dict:
         "unit": "GB/s",
         "ms_per_step": round(kern_ms, 6),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 6),
-        # raw and 'auto' gathers copy bytes; the fp8 paths decode and scale in fp32
-        "dtype": "u8" if wl.kind in (workloads.RAW, workloads.DEQUANT_AUTO) else "f32",
-        "config": {"workload": wl.name, "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
-                   "block_size": wl.block_size, "entry": wl.entry,
-                   "num_blocks": wl.num_blocks, "kind": wl.kind,
-                   "algorithmic_bytes_per_step": alg_bytes,
-                   "parallelism": "single GPU"},
+        # raw, 'auto' and indexer gathers copy bytes; the fp8 paths decode and scale in fp32
+        "dtype": "u8" if wl.kind in (workloads.RAW, workloads.DEQUANT_AUTO, workloads.INDEXER)
+        else "f32",
+        "config": workload_config(wl, alg_bytes),
         "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
         "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
         "per_launch_us": round(kern_ms * 1e3, 3),
@@ -365,6 +420,21 @@ def measure(wl, dev, args) -> dict:
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(wl.name)},
     }
+
+
+def workload_config(wl, alg_bytes: int) -> dict:
+    """The bench line's config object for workload `wl`."""
+    import workloads
+
+    if wl.kind == workloads.INDEXER:
+        return {"workload": wl.name, "num_batches": wl.num_batches, "num_tokens": wl.num_tokens,
+                "block_size": wl.block_size, "head_dim": wl.head_dim,
+                "layout": INDEXER_LAYOUT_NAMES[wl.layout], "num_blocks": wl.num_blocks,
+                "block_stride": wl.block_stride, "kind": wl.kind,
+                "algorithmic_bytes_per_step": alg_bytes, "parallelism": "single GPU"}
+    return {"workload": wl.name, "num_reqs": wl.num_reqs, "num_tokens": wl.num_tokens,
+            "block_size": wl.block_size, "entry": wl.entry, "num_blocks": wl.num_blocks,
+            "kind": wl.kind, "algorithmic_bytes_per_step": alg_bytes, "parallelism": "single GPU"}
 
 
 # --kind of a custom workload -> the workload kind (entry point and conversion)
@@ -466,7 +536,8 @@ def main():
         return
 
     head = measure(wl, dev, args)
-    payload_each_way = wl.gathered_rows() * wl.entry * wl.dst_elem_bytes
+    payload_each_way = (wl.gathered_rows() * (wl.head_dim + 4) if wl.kind == workloads.INDEXER
+                        else wl.gathered_rows() * wl.entry * wl.dst_elem_bytes)
     copy_ref = copy_reference(payload_each_way, dev, args.steps, 3 << 30)
     log(f"[bench] device copy reference {copy_ref['gbs']:.0f} GB/s")
     also = None

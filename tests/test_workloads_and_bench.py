@@ -177,3 +177,34 @@ def test_bench_defaults_name_both_single_request_gathers():
     assert bench.DEFAULT_WORKLOAD == "single_300k_fp8_upconvert"
     assert bench.SECOND_WORKLOAD == "single_60k_raw"
     assert set(workloads.NAMED) >= {bench.DEFAULT_WORKLOAD, bench.SECOND_WORKLOAD}
+
+
+@pytest.mark.parametrize("name,parts", [("indexer_tiny_flat", 4), ("indexer_skew8_tiled", 16)])
+def test_threaded_indexer_oracle_matches_oracle(name, parts):
+    """The indexer CPU baseline's row-range split (token_to_seq and the
+    destinations from r0 on, cu_seqlen shifted by r0) reproduces the oracle's
+    output of the whole gather, including rows claiming another batch."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    sys.path.insert(0, REPO)
+    import bench
+
+    iw = workloads.named(name)
+    iw.token_to_seq[::97] = -1
+    iw.token_to_seq[1::89] = 0
+    want_v, want_s, rows = oracle.run_indexer_workload(iw)
+    v, s = iw.fresh_values(), iw.fresh_scales()
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        got = bench.indexer_oracle_threaded(iw, parts, v, s)(pool)
+    assert got == rows
+    assert torch.equal(v, want_v) and torch.equal(s.view(torch.uint8), want_s.view(torch.uint8))
+
+
+def test_indexer_workload_shapes():
+    iw = workloads.named("indexer_single_300k_flat")
+    assert (iw.num_tokens, iw.block_size, iw.head_dim, iw.block_stride) == (307200, 64, 128, 64 * 132)
+    assert iw.num_blocks == 6000 and iw.gathered_rows() == 307200
+    assert iw.algorithmic_bytes() == 307200 * (2 * 132 + 4) + 8
+    iw = workloads.named("indexer_skew8_tiled")
+    assert iw.num_tokens == sum(workloads.SKEW8_LENS) + 8
+    assert iw.token_to_seq[-8:].tolist() == [-1] * 8
