@@ -204,7 +204,8 @@ def cold_latency(wl_dev, reps: int, scrub_bytes: int = 1 << 30):
     Infinity Cache) with a fill kernel, bracketed by events on the launch stream."""
     import torch
 
-    scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=wl_dev.workspace.device)
+    dev = wl_dev.cache.device if hasattr(wl_dev, "cache") else wl_dev.workspace.device
+    scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=dev)
     run = call_for(wl_dev, getattr(wl_dev, "workspace", None))
     out = []
     for i in range(reps + 3):

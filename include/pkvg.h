@@ -82,6 +82,8 @@ extern "C" {
                            token stride + row bytes); or num_tokens / block_size + 2 * num_reqs
                            >= 2^31 */
 #define PKVG_E_HIP 6    /* a HIP runtime call failed (launch or allocation); see pkvg_last_hip_error */
+#define PKVG_E_SCRATCH 7 /* gather_maybe_dequant_noalloc: the batch needs more task-table scratch than
+                            its fixed array holds (PKVG_NOALLOC_MAX_* below) */
 
 /* kv_cache_dtype values for gather_maybe_dequant */
 #define PKVG_KV_AUTO 0     /* cache holds bf16 entries: bit copy into the bf16 destination */
@@ -156,6 +158,44 @@ int gather_maybe_dequant(const void *src_cache, int32_t kv_cache_dtype,
                          const int32_t *cu_seq_lens, int32_t cu_terminal,
                          const int32_t *seq_starts,
                          int32_t num_reqs, const float *scale, void *stream);
+
+/*
+ * gather_maybe_dequant_noalloc -- gather_maybe_dequant for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and errors
+ * as gather_maybe_dequant, and it calls no hipMalloc, hipFree, stream-ordered
+ * allocator or other allocating routine.
+ *
+ * Batches of at most PKVG_FUSED_MAX_REQS requests use no scratch (as in
+ * gather_maybe_dequant).  Larger batches keep their page-task table (the
+ * exclusive page-count prefix, a task count and one 32-byte record per task
+ * unit) in a fixed array inside the library's device code instead of a
+ * stream-ordered allocation: room for at most PKVG_NOALLOC_MAX_REQS requests
+ * and PKVG_NOALLOC_MAX_TASKS task units (8.25 MiB in all; a task unit holds up to 16
+ * tokens of 1152-byte bf16 rows in such batches, so about four million such
+ * tokens).  A batch beyond that returns PKVG_E_SCRATCH before anything is
+ * enqueued.  Each device the library runs on holds its own copy of the array
+ * until the process ends; its address is looked up on the first call on that
+ * device (hipGetSymbolAddress, not an allocation).
+ *
+ * All calls on one device share that array, which keeps the last call's
+ * contents (every entry a call reads, it has written first).  Calls that can
+ * overlap on one device -- on different streams, or from different threads
+ * without ordering -- race on it and must not be issued; calls ordered on one
+ * stream are safe.
+ */
+#define PKVG_NOALLOC_MAX_REQS 65535
+#define PKVG_NOALLOC_MAX_TASKS 262144
+
+int gather_maybe_dequant_noalloc(const void *src_cache, int32_t kv_cache_dtype,
+                                 int64_t num_blocks, int32_t block_size, int32_t entry,
+                                 int64_t src_block_stride, int64_t src_token_stride,
+                                 void *dst, int64_t num_tokens, int64_t dst_row_stride,
+                                 const int32_t *block_table, int32_t block_table_width,
+                                 int64_t block_table_ld,
+                                 const int32_t *cu_seq_lens, int32_t cu_terminal,
+                                 const int32_t *seq_starts,
+                                 int32_t num_reqs, const float *scale, void *stream);
 
 /*
  * gather_upconvert_fp8 -- fp8 (OCP e4m3fn) cache to bf16 destination (the

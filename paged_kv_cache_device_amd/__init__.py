@@ -47,6 +47,9 @@ PKVG_E_STRIDE = 3
 PKVG_E_DTYPE = 4
 PKVG_E_LIMIT = 5
 PKVG_E_HIP = 6
+PKVG_E_SCRATCH = 7
+PKVG_NOALLOC_MAX_REQS = 65535
+PKVG_NOALLOC_MAX_TASKS = 262144
 PKVG_KV_AUTO = 0
 PKVG_KV_FP8_E4M3 = 1
 PKVG_TASK_INTS = 8
@@ -68,6 +71,7 @@ _CACHE_ARGS = [_i64, _i32, _i32, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _
 SIGNATURES = {
     "gather_cache": [_vp, _i32] + _CACHE_ARGS + [_vp],
     "gather_maybe_dequant": [_vp, _i32] + _CACHE_ARGS + [_vp, _vp],
+    "gather_maybe_dequant_noalloc": [_vp, _i32] + _CACHE_ARGS + [_vp, _vp],
     "gather_upconvert_fp8": [_vp] + _CACHE_ARGS + [_vp, _vp],
     "gather_page_tasks": [_vp, _i32, _vp, _i32, _i64, _i32, _vp, _i32, _i64, _i64, _vp, _i64, _vp,
                           _vp],
@@ -249,7 +253,8 @@ def _scale_tensor(scale, dst: torch.Tensor) -> torch.Tensor:
 
 
 def _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size, kv_cache_dtype,
-                           scale, seq_starts, stream, cu_terminal=None):
+                           scale, seq_starts, stream, cu_terminal=None,
+                           entry_point="gather_maybe_dequant"):
     if dst.dtype != torch.bfloat16:
         raise TypeError("gather_maybe_dequant writes a bf16 destination")
     if kv_cache_dtype == "auto":
@@ -263,8 +268,8 @@ def _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size,
         raise ValueError(f"unknown kv_cache_dtype {kv_cache_dtype!r}")
     args = _cache_args(src_cache, dst, block_table, cu_seq_lens, batch_size, seq_starts,
                        cu_terminal)
-    return PreparedCall("gather_maybe_dequant", [_ptr(src_cache), code, *args, _ptr(sc),
-                                                 _stream_handle() if stream is None else stream])
+    return PreparedCall(entry_point, [_ptr(src_cache), code, *args, _ptr(sc),
+                                      _stream_handle() if stream is None else stream])
 
 
 def _prepare_upconvert(src_cache, dst, block_table, cu_seq_lens, batch_size, scale, seq_starts,
@@ -296,6 +301,20 @@ def gather_maybe_dequant(src_cache: torch.Tensor, dst: torch.Tensor, block_table
     'fp8' dequantises e4m3fn codes with the per-tensor fp32 ``scale``."""
     _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size, kv_cache_dtype,
                            scale, seq_starts, None, cu_terminal)()
+
+
+def gather_maybe_dequant_noalloc(src_cache: torch.Tensor, dst: torch.Tensor,
+                                 block_table: torch.Tensor, cu_seq_lens: torch.Tensor,
+                                 batch_size: int, kv_cache_dtype: str,
+                                 scale: torch.Tensor | None = None,
+                                 seq_starts: torch.Tensor | None = None, *,
+                                 cu_terminal: bool | None = None) -> None:
+    """``gather_maybe_dequant`` that allocates nothing: batches of more than
+    1,024 requests keep their task table in the library's fixed device array
+    (calls that overlap on one device race on it; see include/pkvg.h)."""
+    _prepare_maybe_dequant(src_cache, dst, block_table, cu_seq_lens, batch_size, kv_cache_dtype,
+                           scale, seq_starts, None, cu_terminal,
+                           entry_point="gather_maybe_dequant_noalloc")()
 
 
 def gather_upconvert_fp8(src_cache: torch.Tensor, dst: torch.Tensor, block_table: torch.Tensor,

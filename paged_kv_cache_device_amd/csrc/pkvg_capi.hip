@@ -11,6 +11,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
+// Scratch of the no-allocation entry point (gather_maybe_dequant_noalloc):
+// room for the task table of a batch of up to 65,535 requests and 262,144
+// task units (P and count: 260 KiB; records: 8 MiB).  Each device the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not a device address: its device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t(260) << 10) + (size_t(8) << 20);
+static_assert(kNoAllocScratchBytes >= 4 * (size_t(PKVG_NOALLOC_MAX_REQS) + 2) + 255 + 32 * size_t(PKVG_NOALLOC_MAX_TASKS),
+              "the scratch holds the header's largest task table");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
 
 using pkvg::GatherParams;
@@ -218,33 +232,80 @@ void finish_plan(Plan& pl) {
   pl.shape = shape_for(pl);
 }
 
-int run_plan(Plan& pl, hipStream_t stream) {
+// Task-table scratch of a large batch: P[R+1] | count | (256-byte aligned) records[capacity].
+size_t table_records_offset(int32_t R) { return (sizeof(int32_t) * (size_t(R) + 2) + 255) / 256 * 256; }
+
+size_t table_scratch_bytes(const Plan& pl) {
+  return table_records_offset(pl.p.num_reqs) + sizeof(TaskRecord) * size_t(pl.capacity);
+}
+
+// A large batch: the builder writes its task table into `table_mem` (every field
+// the gather reads is written first, so nothing needs clearing), then the
+// gather reads it.
+hipError_t run_tabled(Plan& pl, void* table_mem, hipStream_t stream) {
+  const int32_t R = pl.p.num_reqs;
+  int32_t* P = static_cast<int32_t*>(table_mem);
+  int32_t* count = P + R + 1;
+  TaskRecord* rec = reinterpret_cast<TaskRecord*>(static_cast<char*>(table_mem) + table_records_offset(R));
+  hipError_t e = build_tasks(pl.p, P, count, rec, pl.capacity, stream);
+  if (e != hipSuccess) return e;
+  pl.p.tasks = rec;
+  pl.p.task_count = count;
+  pl.p.task_capacity = static_cast<int32_t>(pl.capacity);
+  return dispatch(pl, 0, stream);
+}
+
+// Runs a prepared plan.  Batches of at most PKVG_FUSED_MAX_REQS requests need
+// no scratch; larger ones use `fixed_scratch` when given (at least
+// table_scratch_bytes(pl) bytes), else a stream-ordered allocation.
+int run_plan(Plan& pl, hipStream_t stream, void* fixed_scratch = nullptr) {
   const int32_t R = pl.p.num_reqs;
   if (R <= PKVG_FUSED_MAX_REQS) {
     const size_t lds = R <= pkvg::kWaveMaxReqs ? 0 : sizeof(int32_t) * (3 * size_t(R) + 3);
     hipError_t e = dispatch(pl, lds, stream);
     return e == hipSuccess ? PKVG_OK : hip_fail(e);
   }
-  // large batch: stream-ordered scratch = P[R+1] | count | records[capacity]
-  const size_t p_bytes = sizeof(int32_t) * (size_t(R) + 2);
-  const size_t rec_off = (p_bytes + 255) / 256 * 256;
-  const size_t bytes = rec_off + sizeof(TaskRecord) * size_t(pl.capacity);
-  void* scratch = nullptr;
-  hipError_t e = hipMallocAsync(&scratch, bytes, stream);
-  if (e != hipSuccess) return hip_fail(e);
-  int32_t* P = static_cast<int32_t*>(scratch);
-  int32_t* count = P + R + 1;
-  TaskRecord* rec = reinterpret_cast<TaskRecord*>(static_cast<char*>(scratch) + rec_off);
-  e = build_tasks(pl.p, P, count, rec, pl.capacity, stream);
-  if (e == hipSuccess) {
-    pl.p.tasks = rec;
-    pl.p.task_count = count;
-    pl.p.task_capacity = static_cast<int32_t>(pl.capacity);
-    e = dispatch(pl, 0, stream);
+  if (fixed_scratch) {
+    const hipError_t e = run_tabled(pl, fixed_scratch, stream);
+    return e == hipSuccess ? PKVG_OK : hip_fail(e);
   }
-  const hipError_t ef = hipFreeAsync(scratch, stream);
+  void* table_mem = nullptr;
+  hipError_t e = hipMallocAsync(&table_mem, table_scratch_bytes(pl), stream);
+  if (e != hipSuccess) return hip_fail(e);
+  e = run_tabled(pl, table_mem, stream);
+  const hipError_t ef = hipFreeAsync(table_mem, stream);
   if (e != hipSuccess) return hip_fail(e);
   if (ef != hipSuccess) return hip_fail(ef);
+  return PKVG_OK;
+}
+
+// ---------------------------------------------------------------------------
+// the no-allocation entry point's scratch: a fixed device array
+// ---------------------------------------------------------------------------
+
+// The fixed array `scratch` (above the anonymous namespace) holds the table.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`.  Calls no allocating routine.
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return PKVG_E_LIMIT;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e);
+      if (!p) return hip_fail(hipErrorInvalidSymbol);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return PKVG_OK;
 }
 
@@ -653,6 +714,28 @@ int gather_maybe_dequant(const void* src_cache, int32_t kv_cache_dtype, int64_t 
   return run_call(PKVG_OP_GATHER_MAYBE_DEQUANT, kv_cache_dtype, a, scale, stream);
 }
 
+int gather_maybe_dequant_noalloc(const void* src_cache, int32_t kv_cache_dtype, int64_t num_blocks,
+                                 int32_t block_size, int32_t entry, int64_t src_block_stride,
+                                 int64_t src_token_stride, void* dst, int64_t num_tokens,
+                                 int64_t dst_row_stride, const int32_t* block_table, int32_t block_table_width,
+                                 int64_t block_table_ld, const int32_t* cu_seq_lens, int32_t cu_terminal,
+                                 const int32_t* seq_starts, int32_t num_reqs, const float* scale, void* stream) {
+  const GatherArgs a{src_cache, num_blocks, block_size, entry, src_block_stride, src_token_stride, dst,
+                     num_tokens, dst_row_stride, block_table, block_table_width, block_table_ld,
+                     cu_seq_lens, cu_terminal, seq_starts, num_reqs};
+  Plan pl;
+  bool nothing;
+  int st = prepare(PKVG_OP_GATHER_MAYBE_DEQUANT, kv_cache_dtype, a, scale, pl, &nothing);
+  if (st != PKVG_OK || nothing) return st;
+  void* sp = nullptr;
+  if (num_reqs > PKVG_FUSED_MAX_REQS) {
+    if (num_reqs > PKVG_NOALLOC_MAX_REQS || pl.capacity > PKVG_NOALLOC_MAX_TASKS) return PKVG_E_SCRATCH;
+    st = scratch_for_current_device(&sp);
+    if (st != PKVG_OK) return st;
+  }
+  return run_plan(pl, static_cast<hipStream_t>(stream), sp);
+}
+
 int gather_upconvert_fp8(const void* src_cache, int64_t num_blocks, int32_t block_size, int32_t entry,
                          int64_t src_block_stride, int64_t src_token_stride, void* dst, int64_t num_tokens,
                          int64_t dst_row_stride, const int32_t* block_table, int32_t block_table_width,
@@ -721,12 +804,12 @@ int gather_page_tasks(const int32_t* cu_seq_lens, int32_t cu_terminal, const int
   p.task_tokens_magic = magic_for(static_cast<uint32_t>(block_size));
   p.split_shift = 0;
   p.num_tokens = num_tokens;
-  void* scratch = nullptr;
-  hipError_t e = hipMallocAsync(&scratch, sizeof(int32_t) * (size_t(num_reqs) + 1), s);
+  void* prefix_mem = nullptr;
+  hipError_t e = hipMallocAsync(&prefix_mem, sizeof(int32_t) * (size_t(num_reqs) + 1), s);
   if (e != hipSuccess) return hip_fail(e);
-  e = build_tasks(p, static_cast<int32_t*>(scratch), num_tasks, reinterpret_cast<TaskRecord*>(tasks), capacity,
-                  s);
-  const hipError_t ef = hipFreeAsync(scratch, s);
+  e = build_tasks(p, static_cast<int32_t*>(prefix_mem), num_tasks, reinterpret_cast<TaskRecord*>(tasks),
+                  capacity, s);
+  const hipError_t ef = hipFreeAsync(prefix_mem, s);
   if (e != hipSuccess) return hip_fail(e);
   if (ef != hipSuccess) return hip_fail(ef);
   return PKVG_OK;
@@ -741,6 +824,8 @@ const char* pkvg_status_string(int status) {
     case PKVG_E_DTYPE: return "PKVG_E_DTYPE: unsupported element size, kv_cache_dtype or record layout";
     case PKVG_E_LIMIT: return "PKVG_E_LIMIT: beyond an implementation limit";
     case PKVG_E_HIP: return "PKVG_E_HIP: a HIP runtime call failed";
+    case PKVG_E_SCRATCH:
+      return "PKVG_E_SCRATCH: the batch's task table exceeds the no-allocation entry point's fixed scratch";
     default: return "unknown pkvg status";
   }
 }

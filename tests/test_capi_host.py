@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert pkvg.status_string(code).startswith("PKVG_")
     assert "unknown" in pkvg.status_string(99)
     assert lib.pkvg_last_hip_error() == 0
@@ -175,3 +175,18 @@ def _ix(lib, **kw):
 ])
 def test_indexer_argument_checks(lib, kw, code):
     assert _ix(lib, **kw) == code
+
+
+def test_noalloc_rejects_batches_beyond_its_scratch(lib):
+    """The no-allocation entry point checks its fixed scratch's limits before
+    any HIP call: too many requests, or too many task units."""
+    def call(R, T, bs):
+        return lib.gather_maybe_dequant_noalloc(FAKE, pkvg.PKVG_KV_AUTO, 10 ** 6, bs, 576, bs * 576,
+                                                576, FAKE, T, 576, FAKE, 4, 4, FAKE, 1, None, R,
+                                                None, None)
+    assert call(pkvg.PKVG_NOALLOC_MAX_REQS + 1, 10 ** 6, 64) == pkvg.PKVG_E_SCRATCH
+    assert call(2000, 64 * 16 * pkvg.PKVG_NOALLOC_MAX_TASKS, 64) == pkvg.PKVG_E_SCRATCH
+    # argument errors still come first
+    assert lib.gather_maybe_dequant_noalloc(FAKE, 9, 100, 64, 576, 64 * 576, 576, FAKE, 10, 576,
+                                            FAKE, 4, 4, FAKE, 1, None, 2000, None,
+                                            None) == pkvg.PKVG_E_DTYPE

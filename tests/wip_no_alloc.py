@@ -1,0 +1,70 @@
+"""gather_maybe_dequant_noalloc (the entry point that allocates nothing)
+against gather_maybe_dequant, byte for byte, through the C ABI: two calls in a
+row on batches beyond the fused limit (its fixed scratch holds their task
+tables), the second smaller than the first, both cache kinds, and a batch
+within the fused limit (no scratch)."""
+import pytest
+import torch
+
+import paged_kv_cache_device_amd as pkvg
+import workloads
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkvg.library()
+
+
+def batch(R, seed, kind, bs=16, max_len=90):
+    g = torch.Generator("cpu").manual_seed(seed)
+    lens = torch.randint(0, max_len, (R,), generator=g)
+    lens[torch.rand(R, generator=g) < 0.1] = 0
+    lens = lens.tolist()
+    starts = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in lens]
+    pages = sum(-(-n // bs) for n in lens)
+    return workloads.make_workload(f"noalloc_{R}_{kind}", kind, lens, bs, 64, pages + 5, seed=seed,
+                                   starts=starts, scale=0.05, workspace_rows=sum(lens) + 4)
+
+
+def both(wl):
+    """(existing entry point's workspace, no-allocation entry point's workspace)."""
+    d = wl.to(DEV)
+    kv = "fp8" if wl.kind == workloads.DEQUANT_FP8 else "auto"
+    sc = d.scale_tensor if kv == "fp8" else None
+    want = d.fresh_workspace()
+    pkvg.gather_maybe_dequant(d.src_cache(), want[: d.num_tokens, : d.entry], d.block_table,
+                              d.cu_seq_lens, d.num_reqs, kv, sc, d.seq_starts)
+    got = d.fresh_workspace()
+    pkvg.gather_maybe_dequant_noalloc(d.src_cache(), got[: d.num_tokens, : d.entry], d.block_table,
+                                      d.cu_seq_lens, d.num_reqs, kv, sc, d.seq_starts)
+    torch.cuda.synchronize()
+    return want.cpu(), got.cpu()
+
+
+@pytest.mark.parametrize("first,second", [
+    ((3000, workloads.DEQUANT_FP8), (1500, workloads.DEQUANT_AUTO)),
+    ((5000, workloads.DEQUANT_AUTO), (1100, workloads.DEQUANT_FP8)),
+    ((2500, workloads.DEQUANT_FP8), (300, workloads.DEQUANT_FP8)),   # then a fused batch
+])
+def test_noalloc_matches_gather_maybe_dequant(first, second):
+    for i, (R, kind) in enumerate((first, second)):
+        wl = batch(R, 9000 + R + i, kind)
+        log(f"[noalloc] call {i + 1}: R={R} kind={kind} T={wl.num_tokens}")
+        want, got = both(wl)
+        assert torch.equal(want.view(torch.uint8), got.view(torch.uint8)), (R, kind)
+        assert not bool((want.view(torch.uint8) == workloads.SENTINEL_BYTE).all())
+
+
+def test_noalloc_full_size_named_workload():
+    """A named workload at full size through both entry points (fused path)."""
+    wl = workloads.named("mixed_fp8_dequant_strided")
+    log(f"[noalloc] {wl.name} R={wl.num_reqs} T={wl.num_tokens}")
+    want, got = both(wl)
+    assert torch.equal(want.view(torch.uint8), got.view(torch.uint8))
