@@ -11,9 +11,11 @@ written per step / time per step).
 
 Timing: exactly K back-to-back calls bracketed by torch.cuda.synchronize(),
 with one HIP event pair on the launch stream around them.  `value` and
-`ms_per_step` come from the events (the GPU time of the K calls);
+`ms_per_step` come from the events (the GPU time of the K calls); a short spin
+kernel enqueued before the first event keeps the GPU busy while the host
+enqueues the first calls, so the events see the calls back to back.
 `wall_ms_per_step` is the host clock over the same bracket, which adds the two
-synchronisation latencies.  The timed steps rotate over several copies of the
+synchronisation latencies and the spin.  The timed steps rotate over several copies of the
 inputs and outputs whose total is far above the 256 MB Infinity Cache, so no
 step finds its data in a cache.  Printed on stdout: ONE JSON line.  Progress
 goes to stderr.
@@ -35,6 +37,7 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, REPO)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+SPACER_CYCLES = 200_000  # GPU clock cycles of the spin before the timed calls (tens of us)
 METRIC = "effective HBM GB/s (read+write) and % of peak; median gather latency, 1 GPU"
 DEFAULT_WORKLOAD = "single_300k_fp8_upconvert"
 SECOND_WORKLOAD = "single_60k_raw"
@@ -190,6 +193,10 @@ def time_steps(sets, steps: int, warmup: int):
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # a short spin kernel keeps the GPU busy while the host enqueues the first
+    # calls, so the event pair times the calls back to back and not the host's
+    # first submission (the spin lies before e0 and inside the host clock)
+    torch.cuda._sleep(SPACER_CYCLES)
     e0.record()
     for i in range(steps):
         runs[i % len(runs)]()

@@ -335,6 +335,8 @@ int gather_indexer_quant_cache(const void *cache, int64_t num_blocks, int32_t bl
 #define PKVG_TASKS_LDS 1      /* task prefix built in LDS (65..PKVG_FUSED_MAX_REQS requests) */
 #define PKVG_TASKS_TABLE 2    /* task table built by two kernels first (more requests) */
 #define PKVG_TASKS_SINGLE 3   /* one request: no prefix */
+#define PKVG_TASKS_WALK 4     /* the block table walked directly: one workgroup per task unit of each
+                                 table row (batches whose table is about as wide as their pages) */
 
 typedef struct pkvg_plan_info {
   int32_t kernel;        /* PKVG_KERNEL_* */
@@ -348,8 +350,8 @@ typedef struct pkvg_plan_info {
   int32_t task_tokens;   /* tokens per task unit */
   int32_t split_shift;   /* a page is 2^split_shift task units */
   int32_t group_shift;   /* a task unit is 2^group_shift pages */
-  int32_t reserved;      /* 0 */
-  int64_t grid;          /* workgroups launched */
+  int32_t grid_rows;     /* workgroups along y: the requests for PKVG_TASKS_WALK, else 1 */
+  int64_t grid;          /* workgroups launched along x */
   int64_t task_capacity; /* upper bound on the number of task units */
 } pkvg_plan_info;
 

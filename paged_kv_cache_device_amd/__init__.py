@@ -62,6 +62,7 @@ PKVG_TASKS_WAVE = 0
 PKVG_TASKS_LDS = 1
 PKVG_TASKS_TABLE = 2
 PKVG_TASKS_SINGLE = 3
+PKVG_TASKS_WALK = 4
 PKVG_INDEXER_FLAT = 0
 PKVG_INDEXER_TILED = 1
 
@@ -87,11 +88,11 @@ class PlanInfo(ctypes.Structure):
     """pkvg_plan_info of include/pkvg.h."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kernel", "threads", "batch_bytes", "task_mode", "convert", "access_width", "flat",
-        "src_vector", "task_tokens", "split_shift", "group_shift", "reserved")] + [
+        "src_vector", "task_tokens", "split_shift", "group_shift", "grid_rows")] + [
         ("grid", ctypes.c_int64), ("task_capacity", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
-        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 class PkvgError(RuntimeError):

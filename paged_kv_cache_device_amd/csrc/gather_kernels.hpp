@@ -742,7 +742,13 @@ __device__ __forceinline__ void move_page(const GatherParams& p, const PageSrc& 
 
 // Task lookup for one workgroup: in-wave registers (small batches), an LDS
 // prefix, a prebuilt task table (large batches), or one request.
-enum TaskMode : int { kWaveRegs = 0, kLdsPrefix = 1, kTable = 2, kSingle = 3 };
+// kWalk: the table is walked directly -- workgroup (x, y) takes task unit x of
+// request y's block-table row (unit x of the row's columns, whether or not the
+// request's rows reach it), so its table entry and its request's extent are
+// known before any load, as for one request.  Chosen for batches whose table
+// is dense (rows about as wide as their requests' pages), where the units
+// past a request's pages that find nothing to do are few.
+enum TaskMode : int { kWaveRegs = 0, kLdsPrefix = 1, kTable = 2, kSingle = 3, kWalk = 4 };
 
 struct TaskSource {
   int mode;
@@ -750,8 +756,9 @@ struct TaskSource {
   const int32_t* P;
   const int32_t* B;
   const int32_t* S;
-  int32_t b, e, s;         // kSingle: the request's clamped extent and source start
-  int32_t first_phys_raw;  // kSingle: table entry of this workgroup's first task (-1 past the row)
+  int32_t r;               // kSingle, kWalk: the request
+  int32_t b, e, s;         // kSingle, kWalk: the request's clamped extent and source start
+  int32_t first_phys_raw;  // kSingle, kWalk: table entry of this workgroup's first task (-1 past the row)
 };
 
 // Resolve `task` (the same for every lane) to its page, all fields wave-uniform.
@@ -764,6 +771,20 @@ __device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSo
       if (phys >= p.num_blocks) phys = -1;
     } else {
       phys = lookup_block(p, 0, g.logical);
+    }
+    return page_from(p, uniform64(phys < 0 ? -1 : phys), g.pbeg, g.pend, g.out_begin);
+  }
+  if (ts.mode == kWalk) {
+    // task = the unit's index in its table row; j = its index among the request's units
+    const int32_t j = task - static_cast<int32_t>(page_of(p, ts.s));
+    if (j < 0 || j >= page_count(p, ts.b, ts.e, ts.s)) return Page{0, 0, 0};
+    const TaskGeom g = task_geometry(p, j, ts.b, ts.e, ts.s);
+    int64_t phys;
+    if (task == static_cast<int32_t>(blockIdx.x)) {
+      phys = ts.first_phys_raw;
+      if (phys >= p.num_blocks) phys = -1;
+    } else {
+      phys = lookup_block(p, ts.r, g.logical);
     }
     return page_from(p, uniform64(phys < 0 ? -1 : phys), g.pbeg, g.pend, g.out_begin);
   }
@@ -789,20 +810,6 @@ __device__ __forceinline__ Page resolve_task(const GatherParams& p, const TaskSo
                    static_cast<int64_t>(uniform(t.out_begin)));
 }
 
-// The task mode of a launch (low byte of the mode argument).  Each kernel is
-// built twice: for one request, where the mode is the constant kSingle and the
-// other modes' code drops out, and for batches, where the compiler is told it
-// is never kSingle.  Measured on one request against a single build for all
-// modes: 61,440 tokens on 64-token pages 25.2 -> 25.05 us, on 1,024-token
-// pages 25.14 -> 24.92 us.
-template <bool ONE_REQUEST>
-__device__ __forceinline__ int task_mode_of(int32_t mode_arg) {
-  if constexpr (ONE_REQUEST) return kSingle;
-  const int mode = mode_arg & 0xFF;
-  __builtin_assume(mode != kSingle);
-  return mode;
-}
-
 // One int32 read through the vector memory path.  Its wait (vmcnt) leaves the
 // scalar loads in flight alone: scalar loads complete in any order, so waiting
 // for one scalar load waits for all of them, kernel arguments included.
@@ -810,6 +817,48 @@ __device__ __forceinline__ int32_t load_i32_vector_path(const int32_t* q) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(q), 0, 4, kBufferWord3);
   return uniform(__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
 }
+
+// The task mode of a launch (low byte of the mode argument).  Each kernel is
+// built three times: for one request, where the mode is the constant kSingle
+// and the other modes' code drops out; for the table walk, where it is the
+// constant kWalk; and for batches found through a prefix or a task table,
+// where the compiler is told it is neither.  Measured on one request against
+// a single build for all modes: 61,440 tokens on 64-token pages 25.2 -> 25.05
+// us, on 1,024-token pages 25.14 -> 24.92 us.
+enum Build : int { kBuildSingle = 0, kBuildWalk = 1, kBuildPrefix = 2 };
+
+template <int BUILD>
+__device__ __forceinline__ int task_mode_of(int32_t mode_arg) {
+  if constexpr (BUILD == kBuildSingle) return kSingle;
+  if constexpr (BUILD == kBuildWalk) return kWalk;
+  const int mode = mode_arg & 0xFF;
+  __builtin_assume(mode != kSingle && mode != kWalk);
+  return mode;
+}
+
+// The walk's prologue: this workgroup's request is blockIdx.y and its first
+// unit blockIdx.x; the block-table entry at column `lb0` of the request's row
+// (per lane in the group kernel, where lanes without a page of the group pass
+// lane_reads = false), the extent and the start are all requested at once.
+// Every load is unconditional: an always-valid address stands in for an
+// absent one.  Returns the entry read, or -1 past the row.
+__device__ __forceinline__ int32_t walk_prologue(const GatherParams& p, int32_t table_ld, int64_t lb0,
+                                                 bool lane_reads, TaskSource& ts) {
+  const int32_t r = static_cast<int32_t>(blockIdx.y);
+  const bool in_row = lane_reads && lb0 < p.block_table_width;
+  const int32_t* entry_at = in_row ? p.block_table + int64_t(r) * table_ld + lb0 : p.cu_seq_lens;
+  const bool has_end = p.cu_terminal || r + 1 < p.num_reqs;  // else the request ends at num_tokens
+  const int32_t* end_at = p.cu_seq_lens + (has_end ? r + 1 : r);
+  ts.s = p.seq_starts ? load_i32_vector_path(p.seq_starts + r) : 0;
+  const int32_t raw = *entry_at;
+  const int32_t cb = uniform(p.cu_seq_lens[r]);
+  const int32_t ce = uniform(*end_at);
+  ts.r = r;
+  ts.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
+  ts.e = static_cast<int32_t>(clamp_rows(has_end ? ce : p.num_tokens, p.num_tokens));
+  return in_row ? raw : -1;
+}
+
 
 // CONVERT == kCopy: W = bytes per lane access.  CONVERT == kFp8Bf16: W = codes
 // per lane access.  Grid: any size (the host launches one workgroup per task);
@@ -822,11 +871,12 @@ __device__ __forceinline__ int32_t load_i32_vector_path(const int32_t* q) {
 // scalars are preloaded into SGPRs when a wave starts (gfx950 kernarg
 // preloading), so the metadata loads go out without waiting for a kernel
 // argument fetch; the struct arrives while they are in flight.
-template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, bool ONE_REQUEST>
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, int BUILD>
 __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
     const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
     int32_t mode_and_split, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
-    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, GatherParams params) {
+    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, int32_t table_ld,
+    GatherParams params) {
   using M = Mover<CONVERT, W, LAYOUT, SRC_VEC>;
   GatherParams p = params;
   p.cu_seq_lens = cu_seq_lens;
@@ -844,9 +894,9 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
 
   const int32_t R = p.num_reqs;
   TaskSource ts;
-  ts.mode = task_mode_of<ONE_REQUEST>(mode_and_split);
+  ts.mode = task_mode_of<BUILD>(mode_and_split);
   WaveLoads wave_loads{};
-  if constexpr (!ONE_REQUEST) {
+  if constexpr (BUILD == kBuildPrefix) {
     if (ts.mode == kWaveRegs) wave_loads = issue_wave_loads(p);
   }
   int32_t* P = lds;
@@ -857,7 +907,11 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
   ts.S = S;
 
   int32_t num_tasks;
-  if (ts.mode == kSingle) {
+  if (ts.mode == kWalk) {
+    // one workgroup per unit of each table row (grid x by num_reqs)
+    ts.first_phys_raw = uniform(walk_prologue(p, table_ld, blockIdx.x >> p.split_shift, true, ts));
+    num_tasks = static_cast<int32_t>(gridDim.x);
+  } else if (ts.mode == kSingle) {
     // The first task's logical block is (seq_start / task_tokens + blockIdx.x)
     // >> split_shift: its block-table entry is requested together with the
     // request extent instead of after it (one dependent memory round trip
@@ -942,6 +996,15 @@ __device__ __forceinline__ GroupTask group_from(int32_t r, const TaskGeom& g) {
 // and task_tokens = G * block_size gives group-relative token ranges).
 __device__ __forceinline__ GroupTask resolve_group(const GatherParams& p, const TaskSource& ts, int32_t task) {
   if (ts.mode == kSingle) return group_from(0, task_geometry(p, task, ts.b, ts.e, ts.s));
+  if (ts.mode == kWalk) {
+    // task = the group's index in its table row; j = its index among the request's groups
+    const int32_t j = task - static_cast<int32_t>(page_of(p, ts.s));
+    if (j < 0 || j >= page_count(p, ts.b, ts.e, ts.s)) {
+      GroupTask none{};
+      return none;  // gbeg == gend: nothing to move
+    }
+    return group_from(ts.r, task_geometry(p, j, ts.b, ts.e, ts.s));
+  }
   if (ts.mode == kWaveRegs) {
     // (at most R - 1 while task < total; the min keeps every table row in range regardless)
     const int32_t r = min(uniform(static_cast<int32_t>(__popcll(__ballot(ts.wp.incl <= task)))), p.num_reqs - 1);
@@ -1021,11 +1084,12 @@ __device__ __forceinline__ void move_group(const GatherParams& p, int32_t lane_p
 // arguments; `mode_and_group` holds the TaskMode (low byte) and group_shift
 // (the byte above it).  Loads always use flat (row-relative) chunk addressing:
 // each row is addressed on its own.
-template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, bool ONE_REQUEST>
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, int BUILD>
 __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
     const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
     int32_t mode_and_group, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
-    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, GatherParams params) {
+    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, int32_t table_ld,
+    GatherParams params) {
   using M = Mover<CONVERT, W, kFlat, SRC_VEC>;
   GatherParams p = params;
   p.cu_seq_lens = cu_seq_lens;
@@ -1045,10 +1109,11 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
   const int lane = threadIdx.x & 63;
   const int32_t G = 1 << p.group_shift;
   const int32_t R = p.num_reqs;
+  const int32_t first_task = static_cast<int32_t>(blockIdx.x);
   TaskSource ts;
-  ts.mode = task_mode_of<ONE_REQUEST>(mode_and_group);
+  ts.mode = task_mode_of<BUILD>(mode_and_group);
   WaveLoads wave_loads{};
-  if constexpr (!ONE_REQUEST) {
+  if constexpr (BUILD == kBuildPrefix) {
     if (ts.mode == kWaveRegs) wave_loads = issue_wave_loads(p);
   }
   int32_t* P = lds;
@@ -1059,11 +1124,15 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
   ts.S = S;
 
   int32_t num_tasks;
-  if (ts.mode == kSingle) {
+  if (ts.mode == kWalk) {
+    // this workgroup's first group: columns (blockIdx.x << group_shift) + lane of its request's row
+    ts.first_phys_raw = walk_prologue(p, table_ld, (int64_t(blockIdx.x) << p.group_shift) + lane, lane < G, ts);
+    num_tasks = static_cast<int32_t>(gridDim.x);
+  } else if (ts.mode == kSingle) {
     // as in the page kernel: this workgroup's first group's table entries
     // (one per lane) are requested together with the request extent
     ts.s = p.seq_starts ? load_i32_vector_path(p.seq_starts) : 0;
-    const int64_t lp = (static_cast<int64_t>(page_of(p, ts.s) + blockIdx.x) << p.group_shift) + lane;
+    const int64_t lp = (static_cast<int64_t>(page_of(p, ts.s) + first_task) << p.group_shift) + lane;
     const bool in_row = lane < G && lp < p.block_table_width;
     const int32_t* entry_at = in_row ? p.block_table + lp : p.cu_seq_lens;
     const int32_t* end_at = p.cu_seq_lens + p.cu_terminal;
@@ -1089,14 +1158,14 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
     scale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*p.scale)));
 
   const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
-  for (int32_t task = blockIdx.x; task < num_tasks; task += gridDim.x) {
+  for (int32_t task = first_task; task < num_tasks; task += gridDim.x) {
     const GroupTask t = resolve_group(p, ts, task);
     const int32_t rows = t.gend - t.gbeg;
     if (rows <= 0) continue;
     int64_t phys = -1;
     if (lane < G) {
       const int64_t lp = (static_cast<int64_t>(t.unit) << p.group_shift) + lane;
-      if (ts.mode == kSingle && task == static_cast<int32_t>(blockIdx.x)) {
+      if ((ts.mode == kSingle || ts.mode == kWalk) && task == first_task) {
         phys = ts.first_phys_raw;
       } else if (lp < p.block_table_width) {
         phys = p.block_table[static_cast<int64_t>(t.req) * p.block_table_ld + lp];

@@ -65,6 +65,16 @@ struct IndexerParams {
 constexpr int kIndexerThreads = 256;
 constexpr int kIndexerRowsPerWave = 64;
 
+// Where a row's batch extent cu_seqlen[b], cu_seqlen[b + 1] comes from.  The
+// array is loaded together with token_to_seq (one round trip) when it is small
+// enough, instead of after it (a second dependent round trip):
+enum IndexerCuSource : int {
+  kCuWave = 0,    // num_batches + 1 <= 64: lane i of every wave holds cu_seqlen[i]
+  kCuLds = 1,     // num_batches + 1 <= kIndexerLdsCuMax: the workgroup copies it into LDS
+  kCuGlobal = 2,  // larger: each row loads its two entries after its batch id
+};
+constexpr int kIndexerLdsCuMax = 4096;
+
 // Byte offset, inside a record's value area, of chunk j (bytes j*W .. j*W+W-1)
 // of a token whose row starts at `row_base` (flat: slot * HEAD_DIM; tiled: the
 // tile row's start plus the slot's row inside its tile).  A chunk never
@@ -94,8 +104,8 @@ template <> struct IndexerChunk<1> { using T = uint8_t; };
 // striding by the grid's rows.  Source rows are dword-aligned (the host checks
 // the cache base and the record stride; value rows start at multiples of 16
 // bytes inside a record), so bit 0 of a row's address carries its mask when
-// the address crosses lanes.
-template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W>
+// the address crosses lanes.  Dynamic LDS (kCuLds): (num_batches + 1) int32.
+template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W, int CU>
 __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(IndexerParams p) {
   using V = typename IndexerChunk<W>::T;
   constexpr int CPR = HEAD_DIM / W;  // chunks per row
@@ -107,9 +117,20 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
   constexpr int PER_LANE = CPR;
   constexpr int BATCH = PER_LANE < 16 ? PER_LANE : 16;
   static_assert(PER_LANE % BATCH == 0, "whole batches");
+  extern __shared__ int32_t cu_lds[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t stride_rows = int64_t(gridDim.x) * WAVES * kIndexerRowsPerWave;
+  const int32_t ncu = p.num_batches + 1;
+
+  // the batch extents, requested before the first rows' batch ids are needed
+  int32_t cu_lane = 0;
+  if constexpr (CU == kCuWave) {
+    cu_lane = p.cu_seqlen[lane < ncu ? lane : ncu - 1];
+  } else if constexpr (CU == kCuLds) {
+    for (int i = threadIdx.x; i < ncu; i += kIndexerThreads) cu_lds[i] = p.cu_seqlen[i];
+    __syncthreads();
+  }
 
   for (int64_t row0 = (int64_t(blockIdx.x) * WAVES + wave) * kIndexerRowsPerWave; row0 < p.num_tokens;
        row0 += stride_rows) {
@@ -119,8 +140,17 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
     const int32_t batch = p.token_to_seq[ok ? row : p.num_tokens - 1];
     ok = ok && batch >= 0 && batch < p.num_batches;
     const int32_t b = ok ? batch : 0;
-    const int32_t start = p.cu_seqlen[b];
-    const int32_t end = p.cu_seqlen[b + 1];
+    int32_t start, end;
+    if constexpr (CU == kCuWave) {
+      start = __shfl(cu_lane, b, 64);
+      end = __shfl(cu_lane, b + 1, 64);
+    } else if constexpr (CU == kCuLds) {
+      start = cu_lds[b];
+      end = cu_lds[b + 1];
+    } else {
+      start = p.cu_seqlen[b];
+      end = p.cu_seqlen[b + 1];
+    }
     ok = ok && row >= start && row < end;
     const uint32_t pos = ok ? static_cast<uint32_t>(row - start) : 0u;
     const uint32_t col = div_magic(pos, static_cast<uint32_t>(p.block_size), p.block_size_magic);

@@ -34,7 +34,8 @@ static_assert(pkvg::kFusedMaxReqs == PKVG_FUSED_MAX_REQS, "the fused task paths 
 static_assert(pkvg::kIndexerFlat == PKVG_INDEXER_FLAT && pkvg::kIndexerTiled == PKVG_INDEXER_TILED,
               "the header's indexer layout codes are the kernel's");
 static_assert(pkvg::kWaveRegs == PKVG_TASKS_WAVE && pkvg::kLdsPrefix == PKVG_TASKS_LDS &&
-                  pkvg::kTable == PKVG_TASKS_TABLE && pkvg::kSingle == PKVG_TASKS_SINGLE,
+                  pkvg::kTable == PKVG_TASKS_TABLE && pkvg::kSingle == PKVG_TASKS_SINGLE &&
+                  pkvg::kWalk == PKVG_TASKS_WALK,
               "the header's task-mode codes are the kernel's");
 
 thread_local int g_last_hip_error = 0;
@@ -62,8 +63,11 @@ struct Plan {
   int width = 1;          // bytes per lane access (copy) or codes per lane access (fp8)
   int layout = pkvg::kRows;
   bool src_vec = true;
+  int32_t mode = pkvg::kSingle;  // TaskMode
+  int32_t rule_reqs = 1;  // the batch size the unit and shape rules see (1 for a table walk)
   int64_t capacity = 0;   // upper bound on the number of page tasks
-  int64_t grid = 0;       // workgroups launched
+  int64_t grid = 0;       // workgroups launched along x (per table row for a walk)
+  int64_t grid_rows = 1;  // along y: the requests for a walk, else 1
   int shape = 0;          // workgroup shape (ShapeId)
 };
 
@@ -121,40 +125,68 @@ constexpr int64_t kMidMaxPageBytes = 36 * 1024;
 // hipLaunchKernel returns the launch's own status, so the calling thread's
 // error state (which other libraries use) is neither read nor cleared.
 template <typename... Args>
-hipError_t launch(void (*kernel)(Args...), unsigned grid, unsigned block, size_t lds, hipStream_t stream,
+hipError_t launch(void (*kernel)(Args...), dim3 grid, unsigned block, size_t lds, hipStream_t stream,
                   Args... args) {
   void* argv[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), argv, lds, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(block), argv, lds, stream);
 }
 
-// Where the gather kernel finds its page tasks: a prebuilt table, one request,
-// or a prefix built in wave registers (small batches) or LDS.
-int32_t task_mode(const GatherParams& p) {
-  if (p.tasks != nullptr) return pkvg::kTable;
-  if (p.num_reqs == 1) return pkvg::kSingle;
-  return p.num_reqs <= pkvg::kWaveMaxReqs ? pkvg::kWaveRegs : pkvg::kLdsPrefix;
+// Where the gather kernel finds its page tasks: a prebuilt table (large
+// batches), one request, the block table walked directly (batches with a
+// dense table), or a prefix built in wave registers (small batches) or LDS.
+int32_t task_mode(int32_t num_reqs, bool walk) {
+  if (num_reqs > PKVG_FUSED_MAX_REQS && !walk) return pkvg::kTable;
+  if (num_reqs == 1) return pkvg::kSingle;
+  if (walk) return pkvg::kWalk;
+  return num_reqs <= pkvg::kWaveMaxReqs ? pkvg::kWaveRegs : pkvg::kLdsPrefix;
 }
 
-// Each kernel has a build for one request and one for batches (the task mode
-// is then a constant, or known not to be kSingle).
+// Each kernel has a build for one request, one for the table walk and one for
+// the prefix and table modes (the task mode is then a constant, or known to be
+// neither of the others).
+template <int BUILD>
+constexpr bool build_matches(int32_t mode) {
+  return BUILD == pkvg::kBuildSingle ? mode == pkvg::kSingle
+                                     : (BUILD == pkvg::kBuildWalk ? mode == pkvg::kWalk
+                                                                  : mode != pkvg::kSingle && mode != pkvg::kWalk);
+}
+
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, int BUILD>
+hipError_t launch_pages_build(const Plan& pl, size_t lds, hipStream_t stream) {
+  const GatherParams& p = pl.p;
+  return launch(pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, BUILD>,
+                dim3(static_cast<unsigned>(pl.grid), static_cast<unsigned>(pl.grid_rows)), SH::threads, lds,
+                stream, p.cu_seq_lens, p.block_table, p.seq_starts, pl.mode | (p.split_shift << 8), p.num_reqs,
+                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens,
+                static_cast<int32_t>(pl.mode == pkvg::kWalk ? p.block_table_ld : 0), p);
+}
+
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
-hipError_t launch_shape(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  const int32_t mode = task_mode(p);
-  auto kernel = mode == pkvg::kSingle ? pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, true>
-                                      : pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, false>;
-  return launch(kernel, grid, SH::threads, lds, stream, p.cu_seq_lens, p.block_table, p.seq_starts,
-                mode | (p.split_shift << 8), p.num_reqs, p.task_tokens, p.task_tokens_magic,
-                p.block_table_width, p.cu_terminal, p.num_tokens, p);
+hipError_t launch_shape(const Plan& pl, size_t lds, hipStream_t stream) {
+  if (pl.mode == pkvg::kSingle)
+    return launch_pages_build<SH, CONVERT, W, LAYOUT, SRC_VEC, pkvg::kBuildSingle>(pl, lds, stream);
+  if (pl.mode == pkvg::kWalk)
+    return launch_pages_build<SH, CONVERT, W, LAYOUT, SRC_VEC, pkvg::kBuildWalk>(pl, lds, stream);
+  return launch_pages_build<SH, CONVERT, W, LAYOUT, SRC_VEC, pkvg::kBuildPrefix>(pl, lds, stream);
+}
+
+template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, int BUILD>
+hipError_t launch_groups_build(const Plan& pl, size_t lds, hipStream_t stream) {
+  const GatherParams& p = pl.p;
+  return launch(pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, BUILD>,
+                dim3(static_cast<unsigned>(pl.grid), static_cast<unsigned>(pl.grid_rows)), SH::threads, lds,
+                stream, p.cu_seq_lens, p.block_table, p.seq_starts, pl.mode | (p.group_shift << 8), p.num_reqs,
+                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens,
+                static_cast<int32_t>(pl.mode == pkvg::kWalk ? p.block_table_ld : 0), p);
 }
 
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
-hipError_t launch_groups(const GatherParams& p, unsigned grid, size_t lds, hipStream_t stream) {
-  const int32_t mode = task_mode(p);
-  auto kernel = mode == pkvg::kSingle ? pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, true>
-                                      : pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, false>;
-  return launch(kernel, grid, SH::threads, lds, stream, p.cu_seq_lens, p.block_table, p.seq_starts,
-                mode | (p.group_shift << 8), p.num_reqs, p.task_tokens, p.task_tokens_magic,
-                p.block_table_width, p.cu_terminal, p.num_tokens, p);
+hipError_t launch_groups(const Plan& pl, size_t lds, hipStream_t stream) {
+  if (pl.mode == pkvg::kSingle)
+    return launch_groups_build<SH, CONVERT, W, LAYOUT, SRC_VEC, pkvg::kBuildSingle>(pl, lds, stream);
+  if (pl.mode == pkvg::kWalk)
+    return launch_groups_build<SH, CONVERT, W, LAYOUT, SRC_VEC, pkvg::kBuildWalk>(pl, lds, stream);
+  return launch_groups_build<SH, CONVERT, W, LAYOUT, SRC_VEC, pkvg::kBuildPrefix>(pl, lds, stream);
 }
 
 // The workgroup shape of a plan (the rules above; the group kernel always
@@ -164,22 +196,20 @@ int shape_for(const Plan& pl) {
   const int64_t page_out = int64_t(pl.p.task_tokens) * pl.p.row_in_bytes * (pl.convert == pkvg::kFp8Bf16 ? 2 : 1);
   if (page_out <= kSmallMaxPageBytes) return kShapeSmall;
   if (page_out <= kMidMaxPageBytes) return kShapeMid;
-  if (pl.p.num_reqs <= pkvg::kWaveMaxReqs &&
-      (pl.grid >= kWideMinTasks || (pl.convert == pkvg::kFp8Bf16 && pl.layout == pkvg::kFlat)))
+  if (pl.rule_reqs <= pkvg::kWaveMaxReqs &&
+      (pl.grid * pl.grid_rows >= kWideMinTasks || (pl.convert == pkvg::kFp8Bf16 && pl.layout == pkvg::kFlat)))
     return kShapeWide;
   return kShapeNarrow;
 }
 
 template <int CONVERT, int W, int LAYOUT, bool SRC_VEC>
 hipError_t launch_gather(const Plan& pl, size_t lds, hipStream_t stream) {
-  const GatherParams& p = pl.p;
-  const unsigned grid = static_cast<unsigned>(pl.grid);
-  if (p.group_shift > 0) return launch_groups<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+  if (pl.p.group_shift > 0) return launch_groups<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(pl, lds, stream);
   switch (pl.shape) {
-    case kShapeSmall: return launch_shape<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
-    case kShapeMid: return launch_shape<pkvg::Mid, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
-    case kShapeWide: return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
-    default: return launch_shape<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>(p, grid, lds, stream);
+    case kShapeSmall: return launch_shape<pkvg::Small, CONVERT, W, LAYOUT, SRC_VEC>(pl, lds, stream);
+    case kShapeMid: return launch_shape<pkvg::Mid, CONVERT, W, LAYOUT, SRC_VEC>(pl, lds, stream);
+    case kShapeWide: return launch_shape<pkvg::Wide, CONVERT, W, LAYOUT, SRC_VEC>(pl, lds, stream);
+    default: return launch_shape<pkvg::Narrow, CONVERT, W, LAYOUT, SRC_VEC>(pl, lds, stream);
   }
 }
 
@@ -218,17 +248,31 @@ hipError_t dispatch(const Plan& pl, size_t lds, hipStream_t stream) {
 // Builder for large batches and for gather_page_tasks: P scan, then records.
 hipError_t build_tasks(const GatherParams& p, int32_t* P, int32_t* count, TaskRecord* out,
                        int64_t capacity, hipStream_t stream) {
-  hipError_t e = launch(pkvg::scan_page_counts_kernel, 1, pkvg::kScanThreads, 0, stream, p, P, count);
+  hipError_t e = launch(pkvg::scan_page_counts_kernel, dim3(1), pkvg::kScanThreads, 0, stream, p, P, count);
   if (e != hipSuccess || capacity == 0) return e;
   const int64_t blocks = (capacity + 255) / 256;
   const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
-  return launch(pkvg::expand_tasks_kernel, grid, 256, 0, stream, p, const_cast<const int32_t*>(P), out,
+  return launch(pkvg::expand_tasks_kernel, dim3(grid), 256, 0, stream, p, const_cast<const int32_t*>(P), out,
                 static_cast<int32_t>(capacity));
+}
+
+// Task units in one block-table row for a walk: the row's columns split into
+// 2^split_shift parts each, or grouped 2^group_shift at a time.
+int64_t walk_units_per_row(const Plan& pl) {
+  const int64_t w = pl.p.block_table_width;
+  if (pl.p.group_shift > 0) return (w + (int64_t(1) << pl.p.group_shift) - 1) >> pl.p.group_shift;
+  return w << pl.p.split_shift;
 }
 
 // Grid and workgroup shape, once the task units are fixed.
 void finish_plan(Plan& pl) {
-  pl.grid = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
+  if (pl.mode == pkvg::kWalk) {
+    pl.grid = walk_units_per_row(pl);
+    pl.grid_rows = pl.p.num_reqs;
+  } else {
+    pl.grid = pl.capacity < kMaxGrid ? pl.capacity : kMaxGrid;
+    pl.grid_rows = 1;
+  }
   pl.shape = shape_for(pl);
 }
 
@@ -260,8 +304,8 @@ hipError_t run_tabled(Plan& pl, void* table_mem, hipStream_t stream) {
 // table_scratch_bytes(pl) bytes), else a stream-ordered allocation.
 int run_plan(Plan& pl, hipStream_t stream, void* fixed_scratch = nullptr) {
   const int32_t R = pl.p.num_reqs;
-  if (R <= PKVG_FUSED_MAX_REQS) {
-    const size_t lds = R <= pkvg::kWaveMaxReqs ? 0 : sizeof(int32_t) * (3 * size_t(R) + 3);
+  if (pl.mode != pkvg::kTable) {
+    const size_t lds = pl.mode == pkvg::kLdsPrefix ? sizeof(int32_t) * (3 * size_t(R) + 3) : 0;
     hipError_t e = dispatch(pl, lds, stream);
     return e == hipSuccess ? PKVG_OK : hip_fail(e);
   }
@@ -386,10 +430,10 @@ void plan_group(Plan& pl, int64_t row_out_bytes) {
   if (pl.p.split_shift > 0) return;  // units are already parts of a page
   const int32_t bs = pl.p.task_tokens;
   const int64_t page_out = int64_t(bs) * row_out_bytes;
-  const bool batch_or_fp8 = pl.p.num_reqs > 1 || pl.convert == pkvg::kFp8Bf16;
+  const bool batch_or_fp8 = pl.rule_reqs > 1 || pl.convert == pkvg::kFp8Bf16;
   if (page_out > (batch_or_fp8 ? kGroupMaxPageBytesBatchOrFp8 : kGroupMaxPageBytes)) return;
   const int64_t max_group_bytes =
-      pl.p.num_reqs > 1 ? kGroupBatchBytes : (pl.convert == pkvg::kFp8Bf16 ? kSmallMaxPageBytes : kSplitSingleRawBytes);
+      pl.rule_reqs > 1 ? kGroupBatchBytes : (pl.convert == pkvg::kFp8Bf16 ? kSmallMaxPageBytes : kSplitSingleRawBytes);
   int32_t k = 0;
   while (k < kMaxGroupShift && (page_out << (k + 1)) <= max_group_bytes) ++k;
   if (k == 0) return;
@@ -500,6 +544,23 @@ struct GatherArgs {
   int32_t num_reqs;
 };
 
+// Batches whose block table is dense are walked directly (kWalk, one
+// workgroup per unit of each table row): dense when the table's pages are at
+// most 5/4 of the most pages the call's rows can fill, so the workgroups that
+// find no rows stay few.  The y extent of the grid bounds the batch; the table
+// pitch travels as a 32-bit kernel argument.
+constexpr int32_t kMaxWalkReqs = 65535;
+
+bool walk_fits(const GatherArgs& a) {
+  if (a.num_reqs < 2 || a.num_reqs > kMaxWalkReqs || a.block_table_width < 1 || a.block_table_ld > INT32_MAX)
+    return false;
+  const int64_t table_pages = int64_t(a.num_reqs) * a.block_table_width;
+  const int64_t row_pages = a.num_tokens / a.block_size + 2 * int64_t(a.num_reqs) + 1;
+  return table_pages * 4 <= row_pages * 5;
+}
+
+int plan_units(int32_t elem_bytes, const GatherArgs& a, const float* scale, bool walk, Plan& pl);
+
 // Validates a call and plans it (access width, task units, grid, shape);
 // touches no device.  `kind`: elem_bytes (gather_cache) or kv_cache_dtype
 // (gather_maybe_dequant); unused for the upconvert.  `*nothing` is set when
@@ -521,6 +582,20 @@ int prepare(int32_t op, int32_t kind, const GatherArgs& a, const float* scale, P
                         a.cu_seq_lens, a.cu_terminal, a.num_reqs, nothing);
   if (st != PKVG_OK || *nothing) return st;
   if (elem_bytes == 0 && !scale) return PKVG_E_NULL;
+  st = plan_units(elem_bytes, a, scale, walk_fits(a), pl);
+  if (st == PKVG_OK && pl.mode == pkvg::kWalk && walk_units_per_row(pl) > kMaxGrid)
+    st = plan_units(elem_bytes, a, scale, false, pl);  // rows of too many units: not walked
+  if (st != PKVG_OK) return st;
+  finish_plan(pl);
+  return PKVG_OK;
+}
+
+// Fills the plan of a checked call: task mode, access width, task units.
+int plan_units(int32_t elem_bytes, const GatherArgs& a, const float* scale, bool walk, Plan& pl) {
+  pl = Plan{};
+  pl.mode = task_mode(a.num_reqs, walk);
+  pl.rule_reqs = pl.mode == pkvg::kWalk ? 1 : a.num_reqs;
+  int st = PKVG_OK;
   fill_common(pl, a.src, a.dst, a.block_table, a.block_table_width, a.block_table_ld, a.cu_seq_lens,
               a.cu_terminal, a.seq_starts, a.num_reqs, a.num_blocks, a.block_size, a.num_tokens);
   if (elem_bytes > 0) {
@@ -529,20 +604,19 @@ int prepare(int32_t op, int32_t kind, const GatherArgs& a, const float* scale, P
     if (st != PKVG_OK) return st;
     const int64_t row = int64_t(a.entry) * elem_bytes;
     // pl.capacity still counts whole pages here
-    const bool small_unit = a.num_reqs == 1 || (a.num_reqs <= pkvg::kWaveMaxReqs && pl.capacity < kWideMinTasks);
+    const int32_t rr = pl.rule_reqs;
+    const bool small_unit = rr == 1 || (rr <= pkvg::kWaveMaxReqs && pl.capacity < kWideMinTasks);
     plan_split(pl, row,
-               small_unit ? kSplitSingleRawBytes
-                          : (a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchBytes : kSplitAboveBytes));
+               small_unit ? kSplitSingleRawBytes : (rr > pkvg::kWaveMaxReqs ? kSplitBatchBytes : kSplitAboveBytes));
     plan_group(pl, row);
   } else {
     pl.p.scale = scale;
     st = plan_fp8(pl, a.src, a.dst, a.entry, a.src_block_stride, a.src_token_stride, a.dst_row_stride,
                   a.block_size);
     if (st != PKVG_OK) return st;
-    plan_split(pl, 2 * int64_t(a.entry), a.num_reqs > pkvg::kWaveMaxReqs ? kSplitBatchBytes : kSplitAboveBytes);
+    plan_split(pl, 2 * int64_t(a.entry), pl.rule_reqs > pkvg::kWaveMaxReqs ? kSplitBatchBytes : kSplitAboveBytes);
     plan_group(pl, 2 * int64_t(a.entry));
   }
-  finish_plan(pl);
   return PKVG_OK;
 }
 
@@ -585,13 +659,23 @@ bool indexer_structure_supported(int32_t layout, int32_t head_dim, int32_t block
   return false;
 }
 
+template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W>
+hipError_t launch_indexer_cu(const pkvg::IndexerParams& p, unsigned grid, hipStream_t stream) {
+  const int32_t ncu = p.num_batches + 1;
+  if (ncu <= 64)
+    return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuWave>, grid,
+                  pkvg::kIndexerThreads, 0, stream, p);
+  if (ncu <= pkvg::kIndexerLdsCuMax)
+    return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuLds>, grid,
+                  pkvg::kIndexerThreads, sizeof(int32_t) * size_t(ncu), stream, p);
+  return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuGlobal>, grid,
+                pkvg::kIndexerThreads, 0, stream, p);
+}
+
 template <int LAYOUT, int HEAD_DIM, int BT, int HT>
 hipError_t launch_indexer_w(const pkvg::IndexerParams& p, bool vec, unsigned grid, hipStream_t stream) {
-  if (vec)
-    return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, 16>, grid, pkvg::kIndexerThreads, 0,
-                  stream, p);
-  return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, 1>, grid, pkvg::kIndexerThreads, 0,
-                stream, p);
+  if (vec) return launch_indexer_cu<LAYOUT, HEAD_DIM, BT, HT, 16>(p, grid, stream);
+  return launch_indexer_cu<LAYOUT, HEAD_DIM, BT, HT, 1>(p, grid, stream);
 }
 
 template <int LAYOUT, int BT, int HT>
@@ -728,7 +812,7 @@ int gather_maybe_dequant_noalloc(const void* src_cache, int32_t kv_cache_dtype, 
   int st = prepare(PKVG_OP_GATHER_MAYBE_DEQUANT, kv_cache_dtype, a, scale, pl, &nothing);
   if (st != PKVG_OK || nothing) return st;
   void* sp = nullptr;
-  if (num_reqs > PKVG_FUSED_MAX_REQS) {
+  if (pl.mode == pkvg::kTable) {
     if (num_reqs > PKVG_NOALLOC_MAX_REQS || pl.capacity > PKVG_NOALLOC_MAX_TASKS) return PKVG_E_SCRATCH;
     st = scratch_for_current_device(&sp);
     if (st != PKVG_OK) return st;
@@ -764,7 +848,8 @@ int pkvg_plan(int32_t op, int32_t kind, const void* src_cache, int64_t num_block
   info->kernel = pl.p.group_shift > 0 ? PKVG_KERNEL_GROUPS : PKVG_KERNEL_PAGES;
   info->threads = shape_threads(pl.shape);
   info->batch_bytes = shape_threads(pl.shape) * shape_lane_bytes(pl.shape);
-  info->task_mode = num_reqs > PKVG_FUSED_MAX_REQS ? PKVG_TASKS_TABLE : task_mode(pl.p);
+  info->task_mode = pl.mode;
+  info->grid_rows = static_cast<int32_t>(pl.grid_rows);
   info->convert = pl.convert;
   info->access_width = pl.width;
   info->flat = pl.layout == pkvg::kFlat ? 1 : 0;

@@ -180,12 +180,18 @@ def test_indexer_argument_checks(lib, kw, code):
 def test_noalloc_rejects_batches_beyond_its_scratch(lib):
     """The no-allocation entry point checks its fixed scratch's limits before
     any HIP call: too many requests, or too many task units."""
-    def call(R, T, bs):
+    def call(R, T, bs, width):
         return lib.gather_maybe_dequant_noalloc(FAKE, pkvg.PKVG_KV_AUTO, 10 ** 6, bs, 576, bs * 576,
-                                                576, FAKE, T, 576, FAKE, 4, 4, FAKE, 1, None, R,
+                                                576, FAKE, T, 576, FAKE, width, width, FAKE, 1, None, R,
                                                 None, None)
-    assert call(pkvg.PKVG_NOALLOC_MAX_REQS + 1, 10 ** 6, 64) == pkvg.PKVG_E_SCRATCH
-    assert call(2000, 64 * 16 * pkvg.PKVG_NOALLOC_MAX_TASKS, 64) == pkvg.PKVG_E_SCRATCH
+    # sparse tables (far wider than the rows need): the task-table path
+    assert call(pkvg.PKVG_NOALLOC_MAX_REQS + 1, 10 ** 6, 64, 4) == pkvg.PKVG_E_SCRATCH
+    assert call(2000, 64 * 16 * pkvg.PKVG_NOALLOC_MAX_TASKS, 64, 4096) == pkvg.PKVG_E_SCRATCH
+    # a dense table is walked directly and needs no scratch (planned only: no launch here)
+    info = pkvg.pkvg_plan(pkvg.PKVG_OP_GATHER_MAYBE_DEQUANT, pkvg.PKVG_KV_AUTO, FAKE, 10 ** 6, 64, 576,
+                          64 * 576, 576, FAKE, 64 * 16 * pkvg.PKVG_NOALLOC_MAX_TASKS, 576, FAKE, 4, 4,
+                          FAKE, 1, None, 2000, None)
+    assert info["task_mode"] == pkvg.PKVG_TASKS_WALK
     # argument errors still come first
     assert lib.gather_maybe_dequant_noalloc(FAKE, 9, 100, 64, 576, 64 * 576, 576, FAKE, 10, 576,
                                             FAKE, 4, 4, FAKE, 1, None, 2000, None,

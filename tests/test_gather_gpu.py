@@ -785,3 +785,49 @@ def test_concurrent_calls_from_threads():
     for t in threads:
         t.join()
     assert not errors, errors
+
+
+# ---------------------------------------------------------------------------
+# batches walked straight through a dense block table
+# ---------------------------------------------------------------------------
+
+def _walk_cases():
+    W = workloads
+    g = torch.Generator("cpu").manual_seed(31)
+    cases = []
+    # the single-60K bytes over 8 requests (raw), with starts, and fp8 / strided fp8
+    cases.append(W.make_workload("walk_8x7680", W.RAW, [7680] * 8, 64, 576, 1000, seed=41))
+    lens = [300] * 10
+    starts = [int(torch.randint(0, 100, (1,), generator=g)) for _ in lens]
+    cases.append(W.make_workload("walk_starts", W.RAW, lens, 16, 64, 250, seed=42, starts=starts))
+    cases.append(W.make_workload("walk_fp8", W.UPCONVERT, [500, 480, 499, 470], 16, 576, 140, seed=43,
+                                 starts=[7, 0, 16, 33], scale=0.0625))
+    cases.append(W.make_workload("walk_fp8_strided", W.DEQUANT_FP8, [200] * 20, 64, 576, 90, seed=44,
+                                 cache_cols=577, dst_cols=580, scale=0.05, workspace_rows=4004))
+    cases.append(W.make_workload("walk_auto", W.DEQUANT_AUTO, [129] * 40, 32, 576, 200, seed=45))
+    # one-token pages through the group kernel, raw and fp8
+    cases.append(W.make_workload("walk_bs1", W.RAW, [200] * 64, 1, 576, 12900, seed=46))
+    cases.append(W.make_workload("walk_bs1_fp8", W.UPCONVERT, [100] * 30, 1, 576, 3010, seed=47,
+                                 starts=[3] * 30, scale=0.05))
+    cases.append(W.make_workload("walk_bs2", W.RAW, [64, 65, 63, 60] * 16, 2, 64, 2200, seed=48))
+    # beyond the fused batch limit: walked without a task table
+    cases.append(W.make_workload("walk_1500", W.RAW, [40] * 1500, 16, 64, 4600, seed=49))
+    # num_tokens cuts the batch short; open-ended cu_seq_lens; guard-failing entries
+    wl = W.make_workload("walk_clamped", W.RAW, [64] * 12, 16, 64, 60, seed=50, workspace_rows=768)
+    wl.num_tokens = 500
+    cases.append(wl)
+    cases.append(W.make_workload("walk_open", W.RAW, [70] * 6, 16, 64, 40, seed=51,
+                                 workspace_rows=430).open_ended())
+    wl = W.make_workload("walk_guards", W.UPCONVERT, [90] * 9, 16, 64, 60, seed=52, scale=0.05)
+    flat = wl.block_table.view(-1)
+    flat[3], flat[17], flat[30] = -1, wl.num_blocks, wl.num_blocks + 4
+    cases.append(wl)
+    return cases
+
+
+@pytest.mark.parametrize("idx", range(12))
+def test_walk_mode_parity(idx):
+    wl = _walk_cases()[idx]
+    plan = plan_of(wl.to(DEV))
+    assert plan["task_mode"] == pkvg.PKVG_TASKS_WALK, (wl.name, plan)
+    check_parity(wl, DEV)

@@ -175,3 +175,16 @@ def test_indexer_block_addresses_beyond_2_to_31():
     torch.cuda.synchronize()
     assert torch.equal(got_v.cpu(), want_v)
     assert torch.equal(got_s.cpu().view(torch.uint8), want_s.view(torch.uint8))
+
+
+@pytest.mark.parametrize("B", [63, 64, 100, 4095, 4096, 6000])
+def test_indexer_many_batches(B):
+    """Batch extents from wave registers (up to 63 batches), LDS (up to 4,095)
+    and global loads (more): both sides of each switch, with rows claiming
+    other batches and padding rows."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, 40, size=B).tolist()
+    pages = sum(-(-n // 16) for n in lens)
+    iw = workloads.make_indexer_workload(f"ix_batches_{B}", lens, 16, 128, pages + 7, seed=B,
+                                         pad_rows=13, layout=B % 2 * workloads.INDEXER_LAYOUT_TILED)
+    check_indexer_parity(corrupt(iw, rng))

@@ -96,12 +96,48 @@ def test_task_units_and_kernels(op, kind, bs, R, kernel, tokens, split, group, t
 
 
 def test_task_modes():
+    # these tables are as wide as all the rows (sparse): prefix modes by batch size
     assert plan(R=1)["task_mode"] == pkvg.PKVG_TASKS_SINGLE
     assert plan(R=2)["task_mode"] == pkvg.PKVG_TASKS_WAVE
     assert plan(R=64)["task_mode"] == pkvg.PKVG_TASKS_WAVE
     assert plan(R=65)["task_mode"] == pkvg.PKVG_TASKS_LDS
     assert plan(R=1024)["task_mode"] == pkvg.PKVG_TASKS_LDS
     assert plan(R=1025)["task_mode"] == pkvg.PKVG_TASKS_TABLE
+    for p in (plan(R=3), plan(R=100), plan(R=2000)):
+        assert p["grid_rows"] == 1
+
+
+@pytest.mark.parametrize("R,T,bs,width,walk", [
+    (8, 61440, 64, 120, True),       # 8 x 7,680 tokens: a table exactly as wide as the pages
+    (2, 61440, 64, 480, True),
+    (64, 61440, 64, 15, True),
+    (512, 102400, 64, 4, True),      # 512 x 200 tokens: 4 pages a row, 3.1 used
+    (2000, 80000, 16, 3, True),      # beyond the fused limit: walked, no task table
+    (8, 141101, 64, 2048, False),    # skew-8: rows far wider than most requests
+    (64, 298156, 64, 1024, False),   # the mixed batch
+    (8, 61440, 64, 153, False),      # just past 5/4 of the pages
+    (8, 61440, 64, 0, False),        # no columns: nothing to walk
+    (70000, 10 ** 6, 16, 1, False),  # beyond the grid's y extent
+])
+def test_walk_decision(R, T, bs, width, walk):
+    p = plan(R=R, T=T, bs=bs, width=width)
+    if walk:
+        assert p["task_mode"] == pkvg.PKVG_TASKS_WALK and p["grid_rows"] == R, p
+        # one workgroup per unit of each table row: split parts, or groups of pages
+        units = -(-width // (1 << p["group_shift"])) if p["group_shift"] else width << p["split_shift"]
+        assert p["grid"] == units
+    else:
+        assert p["task_mode"] != pkvg.PKVG_TASKS_WALK and p["grid_rows"] == 1, p
+
+
+def test_walk_units_follow_the_single_request_rules():
+    """A walked batch moves the same units as one request: 9 KiB raw units,
+    whole 64-token fp8 pages, 9 KiB groups of one-token raw pages."""
+    assert plan(R=8, width=120)["task_tokens"] == plan(R=1)["task_tokens"] == 8
+    assert plan(op=UP, kind=0, R=8, width=120)["task_tokens"] == 64
+    p = plan(R=512, T=102400, bs=1, width=200)
+    assert (p["task_mode"], p["kernel"], p["group_shift"], p["grid"]) == (
+        pkvg.PKVG_TASKS_WALK, pkvg.PKVG_KERNEL_GROUPS, 3, 25)
 
 
 def test_access_widths():
