@@ -340,6 +340,12 @@ def test_random_page_sizes(seed):
 # zero-length requests, partial pages and guard-skipped pages
 # ---------------------------------------------------------------------------
 
+def sparse_width(lens, bs):
+    """A block-table width four times the longest request's pages (plus 8): far
+    from dense, so a batch takes a prefix mode rather than the table walk."""
+    return 4 * max([-(-n // bs) for n in lens] + [1]) + 8
+
+
 @pytest.mark.parametrize("name,kind,R,bs,mode,unit,split,group", [
     # at most 64 requests and fewer than 1024 whole-page tasks: raw 9 KiB units
     ("small_batch_raw", workloads.RAW, 8, 64, "wave", 8, 3, 0),
@@ -361,8 +367,9 @@ def test_batch_unit_rules(name, kind, R, bs, mode, unit, split, group):
     lens = [0 if ri(0, 7) == 0 else ri(1, max_tokens) for _ in range(R)]
     starts = [ri(0, n // 3) for n in lens]
     pages = sum(-(-n // bs) for n in lens)
+    # a table four times wider than the longest request: the prefix modes, not the walk
     wl = workloads.make_workload(name, kind, lens, bs, 576, pages + 7, seed=R + bs, starts=starts,
-                                 scale=0.05)
+                                 scale=0.05, width=sparse_width(lens, bs))
     flat = wl.block_table.view(-1)
     for _ in range(5):  # guard-skipped pages: past the cache, negative
         flat[ri(0, flat.numel() - 1)] = [wl.num_blocks, -1][ri(0, 1)]
@@ -385,7 +392,7 @@ def test_lds_prefix_share_boundaries(R, kind):
     starts = [ri(0, n // 3) for n in lens]
     pages = sum(-(-n // 16) for n in lens)
     wl = workloads.make_workload(f"lds_share_{R}_{kind}", kind, lens, 16, 576, pages + 5, seed=R,
-                                 starts=starts, scale=0.05)
+                                 starts=starts, scale=0.05, width=sparse_width(lens, 16))
     flat = wl.block_table.view(-1)
     for _ in range(4):
         flat[ri(0, flat.numel() - 1)] = [wl.num_blocks, -1][ri(0, 1)]
