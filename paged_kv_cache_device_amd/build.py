@@ -18,8 +18,8 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # packed fp32 VALU forms stay off: hipcc emits them on its own otherwise
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # the gather kernel's 15 leading scalar argument dwords arrive in SGPRs
-    "-mllvm", "-amdgpu-kernarg-preload-count=15",
+    # the gather kernel's 14 leading scalar argument dwords arrive in SGPRs
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
 ]
 
 

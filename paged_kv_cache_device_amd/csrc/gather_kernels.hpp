@@ -849,10 +849,11 @@ __device__ __forceinline__ int32_t walk_prologue(const GatherParams& p, int32_t 
   const int32_t* entry_at = in_row ? p.block_table + int64_t(r) * table_ld + lb0 : p.cu_seq_lens;
   const bool has_end = p.cu_terminal || r + 1 < p.num_reqs;  // else the request ends at num_tokens
   const int32_t* end_at = p.cu_seq_lens + (has_end ? r + 1 : r);
-  ts.s = p.seq_starts ? load_i32_vector_path(p.seq_starts + r) : 0;
+  // the table entry does not depend on the start, so it goes out first
   const int32_t raw = *entry_at;
   const int32_t cb = uniform(p.cu_seq_lens[r]);
   const int32_t ce = uniform(*end_at);
+  ts.s = p.seq_starts ? load_i32_vector_path(p.seq_starts + r) : 0;
   ts.r = r;
   ts.b = static_cast<int32_t>(clamp_rows(cb, p.num_tokens));
   ts.e = static_cast<int32_t>(clamp_rows(has_end ? ce : p.num_tokens, p.num_tokens));
@@ -861,21 +862,23 @@ __device__ __forceinline__ int32_t walk_prologue(const GatherParams& p, int32_t 
 
 
 // CONVERT == kCopy: W = bytes per lane access.  CONVERT == kFp8Bf16: W = codes
-// per lane access.  Grid: any size (the host launches one workgroup per task);
-// workgroup w takes tasks w, w + gridDim.x, ...  Dynamic LDS (LDS-prefix mode,
-// 64 < num_reqs): (3 * num_reqs + 2) int32.
+// per lane access.  Grid: any size along x (the host launches one workgroup
+// per task); workgroup w takes tasks w, w + gridDim.x, ...; along y, the
+// requests of a table walk (1 otherwise).  Dynamic LDS (LDS-prefix mode, 64 <
+// num_reqs): (3 * num_reqs + 2) int32.
 //
 // The leading scalar arguments repeat the fields of `params` that the task
-// lookup needs first; `mode_and_split` holds the TaskMode the host chose (low
-// byte) and split_shift (the byte above it).  Leading
-// scalars are preloaded into SGPRs when a wave starts (gfx950 kernarg
-// preloading), so the metadata loads go out without waiting for a kernel
-// argument fetch; the struct arrives while they are in flight.
+// lookup needs first (num_tokens as 32 bits, which the host guarantees, and
+// the table pitch, used by the walk); `mode_and_split` holds the TaskMode the
+// host chose (low byte) and split_shift (the byte above it).  These 14 dwords
+// are preloaded into SGPRs when a wave starts (gfx950 kernarg preloading, at
+// most 14 argument dwords), so the metadata loads go out without waiting for
+// a kernel argument fetch; the struct arrives while they are in flight.
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, int BUILD>
 __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
     const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
     int32_t mode_and_split, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
-    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, int32_t table_ld,
+    int32_t block_table_width, int32_t cu_terminal, int32_t num_tokens, int32_t table_ld,
     GatherParams params) {
   using M = Mover<CONVERT, W, LAYOUT, SRC_VEC>;
   GatherParams p = params;
@@ -908,9 +911,10 @@ __global__ __launch_bounds__(SH::threads) void gather_pages_kernel(
 
   int32_t num_tasks;
   if (ts.mode == kWalk) {
-    // one workgroup per unit of each table row (grid x by num_reqs)
+    // one workgroup per unit of each table row (grid x by num_reqs): this
+    // workgroup takes exactly its own unit
     ts.first_phys_raw = uniform(walk_prologue(p, table_ld, blockIdx.x >> p.split_shift, true, ts));
-    num_tasks = static_cast<int32_t>(gridDim.x);
+    num_tasks = static_cast<int32_t>(blockIdx.x) + 1;
   } else if (ts.mode == kSingle) {
     // The first task's logical block is (seq_start / task_tokens + blockIdx.x)
     // >> split_shift: its block-table entry is requested together with the
@@ -1088,7 +1092,7 @@ template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC, int BUILD>
 __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
     const int32_t* cu_seq_lens, const int32_t* block_table, const int32_t* seq_starts,
     int32_t mode_and_group, int32_t num_reqs, int32_t task_tokens, uint32_t task_tokens_magic,
-    int32_t block_table_width, int32_t cu_terminal, int64_t num_tokens, int32_t table_ld,
+    int32_t block_table_width, int32_t cu_terminal, int32_t num_tokens, int32_t table_ld,
     GatherParams params) {
   using M = Mover<CONVERT, W, kFlat, SRC_VEC>;
   GatherParams p = params;
@@ -1127,7 +1131,7 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
   if (ts.mode == kWalk) {
     // this workgroup's first group: columns (blockIdx.x << group_shift) + lane of its request's row
     ts.first_phys_raw = walk_prologue(p, table_ld, (int64_t(blockIdx.x) << p.group_shift) + lane, lane < G, ts);
-    num_tasks = static_cast<int32_t>(gridDim.x);
+    num_tasks = static_cast<int32_t>(blockIdx.x) + 1;  // exactly its own group
   } else if (ts.mode == kSingle) {
     // as in the page kernel: this workgroup's first group's table entries
     // (one per lane) are requested together with the request extent

@@ -157,8 +157,9 @@ hipError_t launch_pages_build(const Plan& pl, size_t lds, hipStream_t stream) {
   return launch(pkvg::gather_pages_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, BUILD>,
                 dim3(static_cast<unsigned>(pl.grid), static_cast<unsigned>(pl.grid_rows)), SH::threads, lds,
                 stream, p.cu_seq_lens, p.block_table, p.seq_starts, pl.mode | (p.split_shift << 8), p.num_reqs,
-                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens,
-                static_cast<int32_t>(pl.mode == pkvg::kWalk ? p.block_table_ld : 0), p);
+                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal,
+                static_cast<int32_t>(p.num_tokens), static_cast<int32_t>(pl.mode == pkvg::kWalk ? p.block_table_ld : 0),
+                p);
 }
 
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
@@ -176,8 +177,9 @@ hipError_t launch_groups_build(const Plan& pl, size_t lds, hipStream_t stream) {
   return launch(pkvg::gather_groups_kernel<SH, CONVERT, W, LAYOUT, SRC_VEC, BUILD>,
                 dim3(static_cast<unsigned>(pl.grid), static_cast<unsigned>(pl.grid_rows)), SH::threads, lds,
                 stream, p.cu_seq_lens, p.block_table, p.seq_starts, pl.mode | (p.group_shift << 8), p.num_reqs,
-                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal, p.num_tokens,
-                static_cast<int32_t>(pl.mode == pkvg::kWalk ? p.block_table_ld : 0), p);
+                p.task_tokens, p.task_tokens_magic, p.block_table_width, p.cu_terminal,
+                static_cast<int32_t>(p.num_tokens), static_cast<int32_t>(pl.mode == pkvg::kWalk ? p.block_table_ld : 0),
+                p);
 }
 
 template <class SH, int CONVERT, int W, int LAYOUT, bool SRC_VEC>
