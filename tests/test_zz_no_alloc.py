@@ -8,7 +8,7 @@ import torch
 
 import paged_kv_cache_device_amd as pkvg
 import workloads
-from gpu_util import log
+from gpu_util import log, plan_of
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +23,9 @@ def _gpu():
 
 
 def batch(R, seed, kind, bs=16, max_len=90):
+    """R requests with a block table twice as wide as the longest needs (a
+    batch past the fused limit with a sparse table takes the task-table path,
+    the one that uses scratch; a dense one would be walked without any)."""
     g = torch.Generator("cpu").manual_seed(seed)
     lens = torch.randint(0, max_len, (R,), generator=g)
     lens[torch.rand(R, generator=g) < 0.1] = 0
@@ -30,7 +33,8 @@ def batch(R, seed, kind, bs=16, max_len=90):
     starts = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in lens]
     pages = sum(-(-n // bs) for n in lens)
     return workloads.make_workload(f"noalloc_{R}_{kind}", kind, lens, bs, 64, pages + 5, seed=seed,
-                                   starts=starts, scale=0.05, workspace_rows=sum(lens) + 4)
+                                   starts=starts, scale=0.05, workspace_rows=sum(lens) + 4,
+                                   width=2 * -(-max_len // bs) + 2)
 
 
 def both(wl):
@@ -56,7 +60,9 @@ def both(wl):
 def test_noalloc_matches_gather_maybe_dequant(first, second):
     for i, (R, kind) in enumerate((first, second)):
         wl = batch(R, 9000 + R + i, kind)
-        log(f"[noalloc] call {i + 1}: R={R} kind={kind} T={wl.num_tokens}")
+        mode = plan_of(wl.to(DEV))["task_mode"]
+        assert mode == (pkvg.PKVG_TASKS_TABLE if R > 1024 else pkvg.PKVG_TASKS_LDS), mode
+        log(f"[noalloc] call {i + 1}: R={R} kind={kind} T={wl.num_tokens} mode={mode}")
         want, got = both(wl)
         assert torch.equal(want.view(torch.uint8), got.view(torch.uint8)), (R, kind)
         assert not bool((want.view(torch.uint8) == workloads.SENTINEL_BYTE).all())
@@ -66,5 +72,17 @@ def test_noalloc_full_size_named_workload():
     """A named workload at full size through both entry points (fused path)."""
     wl = workloads.named("mixed_fp8_dequant_strided")
     log(f"[noalloc] {wl.name} R={wl.num_reqs} T={wl.num_tokens}")
+    want, got = both(wl)
+    assert torch.equal(want.view(torch.uint8), got.view(torch.uint8))
+
+
+def test_noalloc_dense_batch_is_walked():
+    """A dense batch past the fused limit is walked through its table and needs
+    no scratch at all; both entry points agree."""
+    lens = [48] * 1800
+    wl = workloads.make_workload("noalloc_dense", workloads.DEQUANT_FP8, lens, 16, 64, 5500, seed=77,
+                                 scale=0.05)
+    assert plan_of(wl.to(DEV))["task_mode"] == pkvg.PKVG_TASKS_WALK
+    log(f"[noalloc] dense R={wl.num_reqs} T={wl.num_tokens}")
     want, got = both(wl)
     assert torch.equal(want.view(torch.uint8), got.view(torch.uint8))
