@@ -296,6 +296,50 @@ def test_medium_random(seed):
     check_parity(medium_random_workload(seed), DEV)
 
 
+def dense_random_workload(seed: int) -> workloads.Workload:
+    """A seeded batch whose lengths stay within 15% of each other, so its block
+    table is about as wide as its pages and the batch is walked (the host's
+    density rule decides; clamping, starts and narrow tables can tip it back):
+    every page size from one token to 256, raw and fp8 kinds, strided rows,
+    seq_starts, aliased blocks, guard-skipped pages, clamped and open-ended
+    extents, batches past the fused limit."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    kind = [workloads.RAW, workloads.DEQUANT_FP8, workloads.UPCONVERT, workloads.DEQUANT_AUTO][seed % 4]
+    R = [2, 5, 16, 64, 100, 700, 1500][ri(0, 6)]
+    bs = [1, 2, 4, 16, 64, 256][ri(0, 5)]
+    entry = [64, 136, 576][ri(0, 2)]
+    base = max(ri(1, 60_000 // R), 1)
+    lens = [max(base + ri(-base // 8, base // 8), 0) for _ in range(R)]
+    starts = [ri(0, min(n // 8, 3 * bs)) for n in lens] if ri(0, 1) else None
+    pages = sum(-(-n // bs) for n in lens)
+    alias = ri(0, 4) == 0
+    nb = pages + ri(0, 8) if not alias else max([-(-n // bs) for n in lens] + [1]) + 3
+    wl = workloads.make_workload(f"dense_{seed}", kind, lens, bs, entry, max(nb, 1), seed=seed + 91,
+                                 starts=starts, cache_cols=entry + [0, 0, 1, 4][ri(0, 3)],
+                                 dst_cols=entry + [0, 0, 2][ri(0, 2)], scale=[0.0625, 0.05][ri(0, 1)],
+                                 allow_alias=alias)
+    total = int(wl.cu_seq_lens[-1])
+    if ri(0, 5) == 0 and total > 0:
+        T = ri(total * 4 // 5, total)
+        wl.num_tokens = T
+        wl.workspace = wl.workspace[: max(T, 1)].clone()
+    if ri(0, 4) == 0:
+        wl = wl.open_ended()
+    if ri(0, 2) == 0 and wl.block_table.numel() > 0:
+        flat = wl.block_table.view(-1)
+        for _ in range(ri(1, 5)):
+            flat[ri(0, flat.numel() - 1)] = [wl.num_blocks, wl.num_blocks + 9, -1][ri(0, 2)]
+    return wl
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_dense_random(seed):
+    wl = dense_random_workload(30000 + seed)
+    log(f"[dense] seed {30000 + seed}: mode {plan_of(wl.to(DEV))['task_mode']}")
+    check_parity(wl, DEV)
+
+
 def page_size_random_workload(seed: int) -> workloads.Workload:
     """A seeded batch over the whole page-size range: block sizes from 1 to
     1,000 tokens and rows from 1 element to 1,000, so that pages go whole,
