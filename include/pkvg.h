@@ -48,9 +48,11 @@
  *  - All work is enqueued on `stream` (a hipStream_t; NULL is the null
  *    stream) and is asynchronous: nothing synchronises with the host.  The
  *    caller keeps every buffer alive until the stream has passed the work.
- *  - Calls are thread-safe and re-entrant.  Requests with more than
- *    PKVG_FUSED_MAX_REQS entries allocate a stream-ordered scratch buffer
- *    (hipMallocAsync / hipFreeAsync on `stream`); smaller ones allocate nothing.
+ *  - Calls are thread-safe and re-entrant.  Batches of more than
+ *    PKVG_FUSED_MAX_REQS requests allocate a stream-ordered scratch buffer
+ *    (hipMallocAsync / hipFreeAsync on `stream`) unless their block table is
+ *    dense (then the table is walked directly, see PKVG_TASKS_WALK); other
+ *    calls allocate nothing.
  *    A call enqueues kernel launches only (plus that allocation and its free)
  *    and no memset, so it can be captured into a HIP graph; each replay reads
  *    the buffers' contents at replay time.

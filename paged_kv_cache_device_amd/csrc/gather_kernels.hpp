@@ -13,11 +13,13 @@
 //
 // Design for gfx950:
 //  * how a workgroup finds its page depends on the batch: one request needs
-//    no scan (its first block-table entry is fetched with the request extent);
-//    up to 64 requests are scanned in wave registers and found with a ballot;
-//    up to 1024 in LDS with a binary search; more use a task table built by
-//    two small kernels.  Task fields live in SGPRs (readfirstlane), so no
-//    barrier follows the lookup;
+//    no scan (its first block-table entry is fetched with the request extent),
+//    and neither does a batch whose block table is dense (workgroup (x, y)
+//    takes unit x of request y's table row); otherwise up to 64 requests are
+//    scanned in wave registers and found with a ballot, up to 1024 in LDS
+//    with a binary search, and more use a task table built by two small
+//    kernels.  Task fields live in SGPRs (readfirstlane), so no barrier
+//    follows the lookup;
 //  * the hot loop moves 16-byte (dwordx4) chunks, consecutive lanes on
 //    consecutive chunks, so one wave instruction covers 1 KiB of a row span;
 //    a whole page's loads are in flight before the matching stores, with the
