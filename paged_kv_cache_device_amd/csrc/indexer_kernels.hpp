@@ -75,21 +75,23 @@ enum IndexerCuSource : int {
 };
 constexpr int kIndexerLdsCuMax = 4096;
 
-// Byte offset, inside a record's value area, of chunk j (bytes j*W .. j*W+W-1)
-// of a token whose row starts at `row_base` (flat: slot * HEAD_DIM; tiled: the
-// tile row's start plus the slot's row inside its tile).  A chunk never
-// crosses a tile (W divides HT).
+// Byte offset of chunk j (bytes j*W .. j*W+W-1 of a token) from the token's
+// first value byte (indexer_row_base): consecutive in the flat layout; in the
+// tiled one, HT bytes per tile and BT * HT bytes between a row's tiles.  A
+// chunk never crosses a tile (W divides HT).
 template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W>
-__device__ __forceinline__ uint32_t indexer_chunk_offset(uint32_t row_base, uint32_t j) {
+__device__ __forceinline__ uint32_t indexer_chunk_offset(uint32_t j) {
   const uint32_t d = j * W;
   if constexpr (LAYOUT == kIndexerFlat) {
-    return row_base + d;
+    return d;
   } else {
     static_assert(HT % W == 0, "a chunk stays inside one tile");
-    return row_base + (d / HT) * (BT * HT) + d % HT;
+    return (d / HT) * (BT * HT) + d % HT;
   }
 }
 
+// Byte offset of a token's first value byte inside its record: slot * HEAD_DIM
+// (flat), or the start of its tile row plus its row inside the first tile.
 template <int LAYOUT, int HEAD_DIM, int BT, int HT>
 __device__ __forceinline__ uint32_t indexer_row_base(uint32_t slot) {
   if constexpr (LAYOUT == kIndexerFlat) return slot * HEAD_DIM;
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
         const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(src_hi), r, 64));
         take[k] = (lo & 1u) != 0u;
         const uint8_t* q = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | (lo & ~1u));
-        if (take[k]) v[k] = load_stream<V>(q + indexer_chunk_offset<LAYOUT, HEAD_DIM, BT, HT, W>(0u, c % CPR));
+        if (take[k]) v[k] = load_stream<V>(q + indexer_chunk_offset<LAYOUT, HEAD_DIM, BT, HT, W>(c % CPR));
       }
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
