@@ -188,3 +188,47 @@ def test_indexer_many_batches(B):
     iw = workloads.make_indexer_workload(f"ix_batches_{B}", lens, 16, 128, pages + 7, seed=B,
                                          pad_rows=13, layout=B % 2 * workloads.INDEXER_LAYOUT_TILED)
     check_indexer_parity(corrupt(iw, rng))
+
+
+def test_indexer_graph_replays():
+    """The call enqueues one kernel launch and no allocation or memset, so a
+    decode loop can capture it.  Between replays the cache bytes, the
+    token-to-batch ids and the table change in place and eager work runs;
+    each replay must match the oracle on the inputs of that moment."""
+    lens = [700, 0, 130, 2100, 64]
+    pages = sum(-(-n // 64) for n in lens)
+    iw = workloads.make_indexer_workload("ix_graph", lens, 64, 128, pages + 5, seed=31,
+                                         pad_rows=9, layout=workloads.INDEXER_LAYOUT_TILED)
+    d = iw.to(DEV)
+    got_v, got_s = d.fresh_values(), d.fresh_scales()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            run_indexer_hip(d, got_v, got_s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(32)
+    for rep in range(4):
+        log(f"[indexer graph] replay {rep}")
+        fresh = workloads.make_indexer_workload("ix_graph", lens, 64, 128, pages + 5,
+                                                seed=100 + rep, pad_rows=9,
+                                                layout=workloads.INDEXER_LAYOUT_TILED)
+        iw.cache.copy_(fresh.cache)
+        iw.token_to_seq.copy_(fresh.token_to_seq)
+        iw.block_table.copy_(fresh.block_table)
+        if rep >= 2:   # masks of every kind, the table width left as captured
+            width = iw.block_table_width
+            corrupt(iw, rng)
+            iw.block_table_width = width
+        for f in ("cache", "token_to_seq", "block_table"):
+            getattr(d, f).copy_(getattr(iw, f))
+        got_v.fill_(workloads.SENTINEL_BYTE)
+        got_s.view(torch.uint8).fill_(workloads.SENTINEL_BYTE)
+        torch.cuda.synchronize()
+        graph.replay()
+        _ = d.cache.sum()
+        torch.cuda.synchronize()
+        want_v, want_s, _ = oracle.run_indexer_workload(iw)
+        assert torch.equal(got_v.cpu(), want_v), f"replay {rep}: values differ"
+        assert torch.equal(got_s.cpu().view(torch.uint8), want_s.view(torch.uint8)), \
+            f"replay {rep}: scales differ"

@@ -86,3 +86,38 @@ def test_noalloc_dense_batch_is_walked():
     log(f"[noalloc] dense R={wl.num_reqs} T={wl.num_tokens}")
     want, got = both(wl)
     assert torch.equal(want.view(torch.uint8), got.view(torch.uint8))
+
+
+def test_noalloc_graph_replays():
+    """Callers that cannot allocate include graph capture: the scratch path
+    (a sparse batch past the fused limit: task builder, then gather, both on
+    the fixed scratch) is captured once and replayed with new cache contents
+    in place; every replay matches the allocating entry point run eagerly on
+    the inputs of that moment."""
+    wl = batch(2200, 9500, workloads.DEQUANT_FP8)
+    d = wl.to(DEV)
+    assert plan_of(d)["task_mode"] == pkvg.PKVG_TASKS_TABLE
+    got = d.fresh_workspace()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            pkvg.gather_maybe_dequant_noalloc(d.src_cache(), got[: d.num_tokens, : d.entry],
+                                              d.block_table, d.cu_seq_lens, d.num_reqs, "fp8",
+                                              d.scale_tensor, d.seq_starts)
+    torch.cuda.synchronize()
+    base = d.cache_base.view(torch.uint8).clone()
+    for rep in range(3):
+        log(f"[noalloc graph] replay {rep}")
+        d.cache_base.view(torch.uint8).copy_(torch.roll(base, 37 * rep + 1))
+        got.view(torch.uint8).fill_(workloads.SENTINEL_BYTE)
+        torch.cuda.synchronize()
+        graph.replay()
+        _ = d.cache_base.sum()
+        torch.cuda.synchronize()
+        want = d.fresh_workspace()
+        pkvg.gather_maybe_dequant(d.src_cache(), want[: d.num_tokens, : d.entry], d.block_table,
+                                  d.cu_seq_lens, d.num_reqs, "fp8", d.scale_tensor, d.seq_starts)
+        torch.cuda.synchronize()
+        assert torch.equal(want.view(torch.uint8), got.view(torch.uint8)), rep
+        assert not bool((want.view(torch.uint8) == workloads.SENTINEL_BYTE).all())
