@@ -290,8 +290,9 @@ int gather_page_tasks(const int32_t *cu_seq_lens, int32_t cu_terminal, const int
  *                     may be NULL when block_table_width == 0
  *   stream            hipStream_t or NULL
  *
- * Nothing is allocated; one kernel is enqueued.  num_tokens == 0 or
- * num_batches == 0 returns PKVG_OK without enqueueing anything.  Errors
+ * Nothing is allocated; one kernel is enqueued.  num_tokens == 0,
+ * num_batches == 0, num_blocks == 0 or block_table_width == 0 (no row can
+ * pass the masks) returns PKVG_OK without enqueueing anything.  Errors
  * (before anything is enqueued): PKVG_E_NULL, PKVG_E_SHAPE, PKVG_E_STRIDE
  * (also a misaligned cache, record stride or dst_scales), PKVG_E_DTYPE,
  * PKVG_E_LIMIT, PKVG_E_HIP.

@@ -27,9 +27,9 @@
 // the wave moves the 64 rows' value bytes in W-byte chunks, consecutive lanes
 // on consecutive chunks of consecutive rows (a 16-byte chunk per lane puts
 // 1 KiB of contiguous rows under one wave instruction), taking each row's
-// address from its owner lane with a cross-lane read; each lane then moves its
-// own row's 4-byte scale.  Loads of all of a lane's chunks go out before its
-// stores, with the nontemporal policy (each byte is touched once).
+// address from its owner lane with a cross-lane read; each lane also moves its
+// own row's 4-byte scale.  A lane's scale and chunk loads all go out before
+// its stores, with the nontemporal policy (each byte is touched once).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -102,11 +102,27 @@ template <int W> struct IndexerChunk;
 template <> struct IndexerChunk<16> { using T = u32x4; };
 template <> struct IndexerChunk<1> { using T = uint8_t; };
 
+// The cache through a global (address space 1) pointer.  A row's address is
+// rebuilt from halves another lane holds; as a generic pointer its load would
+// be a flat load, which the hardware counts with the LDS operations, so the
+// wait before the next cross-lane read would also wait for that load to
+// return and the wave's loads would go out one round trip at a time.
+typedef const __attribute__((address_space(1))) uint8_t* IndexerCache;
+
+template <typename V>
+__device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) V*>(base + off));
+}
+
 // Grid: any size; wave w of workgroup g takes rows from (g * 4 + w) * 64 on,
 // striding by the grid's rows.  Source rows are dword-aligned (the host checks
 // the cache base and the record stride; value rows start at multiples of 16
-// bytes inside a record), so bit 0 of a row's address carries its mask when
-// the address crosses lanes.  Dynamic LDS (kCuLds): (num_batches + 1) int32.
+// bytes inside a record), so bit 0 of a row's offset carries its mask when
+// the offset crosses lanes.  The host launches only with num_blocks >= 1 and
+// block_table_width >= 1 (otherwise every row is masked): a masked row keeps
+// an offset inside record 0, so every load is in bounds and goes out without
+// a branch, and only the stores are masked.  Dynamic LDS (kCuLds):
+// (num_batches + 1) int32.
 template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W, int CU>
 __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(IndexerParams p) {
   using V = typename IndexerChunk<W>::T;
@@ -162,27 +178,40 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
     if (ok) block = p.block_table[int64_t(b) * p.block_table_ld + col];
     ok = ok && block >= 0 && block < p.num_blocks;
     // clamped to block 0 when invalid, then widened: the record stride is large
-    const int64_t record = int64_t(ok ? block : 0) * p.block_stride;
-    const uint64_t src_bits =
-        reinterpret_cast<uint64_t>(p.cache + record + indexer_row_base<LAYOUT, HEAD_DIM, BT, HT>(slot));
-    const uint32_t src_lo = static_cast<uint32_t>(src_bits) | (ok ? 1u : 0u);
-    const uint32_t src_hi = static_cast<uint32_t>(src_bits >> 32);
+    const IndexerCache cache = (IndexerCache)p.cache;  // an address-space cast: the cache is global memory
+    const uint64_t record = static_cast<uint64_t>(int64_t(ok ? block : 0) * p.block_stride);
+    const uint64_t src_off = record + indexer_row_base<LAYOUT, HEAD_DIM, BT, HT>(slot);
+    const uint32_t off_lo = static_cast<uint32_t>(src_off) | (ok ? 1u : 0u);
+    const uint32_t off_hi = static_cast<uint32_t>(src_off >> 32);
+    uint32_t scale = 0;
 
     // --- value bytes: chunk c = lane + 64k is chunk c % CPR of row c / CPR ---
 #pragma unroll
     for (int k0 = 0; k0 < PER_LANE; k0 += BATCH) {
-      V v[BATCH];
+      // every chunk's row offset first (cross-lane reads), then every load
+      uint64_t off[BATCH];
       bool take[BATCH];
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
         const int r = static_cast<int>(c / CPR);
-        const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(src_lo), r, 64));
-        const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(src_hi), r, 64));
+        const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(off_lo), r, 64));
+        const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(off_hi), r, 64));
         take[k] = (lo & 1u) != 0u;
-        const uint8_t* q = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | (lo & ~1u));
-        if (take[k]) v[k] = load_stream<V>(q + indexer_chunk_offset<LAYOUT, HEAD_DIM, BT, HT, W>(c % CPR));
+        off[k] = ((static_cast<uint64_t>(hi) << 32) | (lo & ~1u)) +
+                 indexer_chunk_offset<LAYOUT, HEAD_DIM, BT, HT, W>(c % CPR);
       }
+      V v[BATCH];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) v[k] = load_cache<V>(cache, off[k]);
+      // the scale of this lane's own row goes out with the first batch's loads
+      if (k0 == 0) scale = load_cache<uint32_t>(cache, record + p.scale_area + slot * 4u);
+      // A use of the first chunk here keeps its load ahead of the stores: the
+      // compiler would otherwise move that load under its store's mask, after
+      // the other loads, and the first store would wait for every load instead
+      // of the first one (measured on 307,200-row gathers: 1-1.5% slower).
+      if constexpr (W == 16) asm volatile("" ::"v"(v[0].x));
+      else asm volatile("" ::"v"(static_cast<uint32_t>(v[0])));
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
@@ -190,11 +219,7 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
         if (take[k]) store_stream(p.dst_values + r * p.dst_value_stride + (c % CPR) * W, v[k]);
       }
     }
-    // --- the scale of this lane's own row ------------------------------------
-    if (ok) {
-      const uint32_t scale = load_stream<uint32_t>(p.cache + record + p.scale_area + slot * 4u);
-      store_stream(p.dst_scales + int64_t(row) * p.dst_scale_stride, scale);
-    }
+    if (ok) store_stream(p.dst_scales + int64_t(row) * p.dst_scale_stride, scale);
   }
 }
 

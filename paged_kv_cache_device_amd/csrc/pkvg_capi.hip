@@ -710,7 +710,9 @@ int prepare_indexer(const void* cache, int64_t num_blocks, int32_t block_size, i
   if (block_stride < record_bytes || dst_value_stride < head_dim || dst_scale_stride < 1 ||
       block_table_ld < block_table_width)
     return PKVG_E_STRIDE;
-  if (num_tokens == 0 || num_batches == 0) {
+  // no row can pass the masks: nothing to enqueue (a launched kernel relies on
+  // record 0 existing, as the address masked rows keep)
+  if (num_tokens == 0 || num_batches == 0 || num_blocks == 0 || block_table_width == 0) {
     *nothing = true;
     return PKVG_OK;
   }

@@ -172,6 +172,9 @@ def _ix(lib, **kw):
     (dict(bstride=1 << 31), pkvg.PKVG_E_LIMIT),
     (dict(T=0, cache=None, vals=None, scales=None, t2s=None, cu=None, table=None), pkvg.PKVG_OK),
     (dict(B=0, cache=None, vals=None, scales=None, t2s=None, cu=None, table=None), pkvg.PKVG_OK),
+    # no row can pass the block-id or column masks: nothing is enqueued
+    (dict(nb=0, cache=None, vals=None, scales=None, t2s=None, cu=None, table=None), pkvg.PKVG_OK),
+    (dict(W=0, cache=None, vals=None, scales=None, t2s=None, cu=None, table=None), pkvg.PKVG_OK),
 ])
 def test_indexer_argument_checks(lib, kw, code):
     assert _ix(lib, **kw) == code
