@@ -114,6 +114,14 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
   return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) V*>(base + off));
 }
 
+// 16-byte chunks are stored through a buffer resource over the wave's own
+// destination rows (fewer than 2^31 bytes: the host checks the row stride).
+// A masked chunk takes an offset past the resource's range, and the hardware
+// drops such a store, so the stores need no branch: without one the compiler
+// keeps every load ahead of the stores and waits for them one by one.
+constexpr uint32_t kIndexerMaskedOffset = 0x80000000u;
+constexpr int32_t kIndexerStorePolicy = 0x02;  // nt: streamed, as the nontemporal stores
+
 // Grid: any size; wave w of workgroup g takes rows from (g * 4 + w) * 64 on,
 // striding by the grid's rows.  Source rows are dword-aligned (the host checks
 // the cache base and the record stride; value rows start at multiples of 16
@@ -121,8 +129,9 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
 // the offset crosses lanes.  The host launches only with num_blocks >= 1 and
 // block_table_width >= 1 (otherwise every row is masked): a masked row keeps
 // an offset inside record 0, so every load is in bounds and goes out without
-// a branch, and only the stores are masked.  Dynamic LDS (kCuLds):
-// (num_batches + 1) int32.
+// a branch, and only the stores are masked.  W == 16 needs dword-aligned
+// destination rows and 64 * dst_value_stride < 2^31 (the host picks W == 1
+// otherwise).  Dynamic LDS (kCuLds): (num_batches + 1) int32.
 template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W, int CU>
 __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(IndexerParams p) {
   using V = typename IndexerChunk<W>::T;
@@ -137,7 +146,8 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
   static_assert(PER_LANE % BATCH == 0, "whole batches");
   extern __shared__ int32_t cu_lds[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform, so a wave's row range and its destination resource sit in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t stride_rows = int64_t(gridDim.x) * WAVES * kIndexerRowsPerWave;
   const int32_t ncu = p.num_batches + 1;
 
@@ -184,6 +194,11 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
     const uint32_t off_lo = static_cast<uint32_t>(src_off) | (ok ? 1u : 0u);
     const uint32_t off_hi = static_cast<uint32_t>(src_off >> 32);
     uint32_t scale = 0;
+    // this wave's destination rows (16-byte chunks): row0 .. row0 + 63, cut at num_tokens
+    const int64_t wave_rows = p.num_tokens - row0 < 64 ? p.num_tokens - row0 : 64;
+    const __amdgpu_buffer_rsrc_t dst_rows = __builtin_amdgcn_make_buffer_rsrc(
+        p.dst_values + row0 * p.dst_value_stride, 0, static_cast<int32_t>(wave_rows * p.dst_value_stride),
+        kBufferWord3);
 
     // --- value bytes: chunk c = lane + 64k is chunk c % CPR of row c / CPR ---
 #pragma unroll
@@ -206,17 +221,27 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
       for (int k = 0; k < BATCH; ++k) v[k] = load_cache<V>(cache, off[k]);
       // the scale of this lane's own row goes out with the first batch's loads
       if (k0 == 0) scale = load_cache<uint32_t>(cache, record + p.scale_area + slot * 4u);
-      // A use of the first chunk here keeps its load ahead of the stores: the
-      // compiler would otherwise move that load under its store's mask, after
-      // the other loads, and the first store would wait for every load instead
-      // of the first one (measured on 307,200-row gathers: 1-1.5% slower).
-      if constexpr (W == 16) asm volatile("" ::"v"(v[0].x));
-      else asm volatile("" ::"v"(static_cast<uint32_t>(v[0])));
+      if constexpr (W == 16) {
 #pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
-        const int64_t r = row0 + static_cast<int64_t>(c / CPR);
-        if (take[k]) store_stream(p.dst_values + r * p.dst_value_stride + (c % CPR) * W, v[k]);
+        for (int k = 0; k < BATCH; ++k) {
+          const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
+          const uint32_t o = take[k] ? (c / CPR) * static_cast<uint32_t>(p.dst_value_stride) + (c % CPR) * W
+                                     : kIndexerMaskedOffset;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_plain, v[k]), dst_rows, o, 0,
+                                                 kIndexerStorePolicy);
+        }
+      } else {
+        // A use of the first chunk keeps its load ahead of the masked stores:
+        // the compiler would otherwise move that load under its store's mask,
+        // after the other loads, and the first store would wait for every
+        // load instead of the first one.
+        asm volatile("" ::"v"(static_cast<uint32_t>(v[0])));
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+          const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
+          const int64_t r = row0 + static_cast<int64_t>(c / CPR);
+          if (take[k]) store_stream(p.dst_values + r * p.dst_value_stride + (c % CPR) * W, v[k]);
+        }
       }
     }
     if (ok) store_stream(p.dst_scales + int64_t(row) * p.dst_scale_stride, scale);

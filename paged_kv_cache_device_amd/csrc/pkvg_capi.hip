@@ -743,8 +743,9 @@ int prepare_indexer(const void* cache, int64_t num_blocks, int32_t block_size, i
   p.block_size = block_size;
   p.block_size_magic = magic_for(static_cast<uint32_t>(block_size));
   p.scale_area = static_cast<uint32_t>(int64_t(block_size) * head_dim);
-  // 16-byte chunks need dword-aligned destination rows (the source rows are)
-  *vec = aligned(dst_values, 4) && dst_value_stride % 4 == 0;
+  // 16-byte chunks need dword-aligned destination rows (the source rows are),
+  // and a wave's 64 rows within the 2^31-byte range of its store resource
+  *vec = aligned(dst_values, 4) && dst_value_stride % 4 == 0 && dst_value_stride < (int64_t(1) << 25);
   return PKVG_OK;
 }
 
