@@ -180,9 +180,48 @@ constexpr int32_t kPolicyDeviceStream = 0x12;
 
 typedef uint32_t u32x4_plain __attribute__((ext_vector_type(4)));
 
+// Plain streaming (nt) policy of the buffer store builtins.
+constexpr int32_t kPolicyStream = 0x02;
+
 // A 16-byte device-scope streaming store at byte `off` of a buffer resource.
 __device__ __forceinline__ void store_write_through(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4_plain& v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolicyDeviceStream);
+}
+
+typedef uint32_t u32x2_plain __attribute__((ext_vector_type(2)));
+
+// A chunk of 1 to 16 bytes stored at byte `off` of a buffer resource with the
+// cache policy POLICY.  The hardware drops a store whose offset lies at or
+// past the resource's range: a lane whose chunk is out of range passes
+// kMaskedOffset (every resource here spans fewer than 2^31 bytes) and is
+// masked without a branch.  Without a branch around the stores the compiler
+// keeps each load ahead of them and waits for each load only before its own
+// store; with one, it can move a load whose only use is the guarded store
+// under the guard, and wait for every load (even every store already issued)
+// before the first.
+constexpr uint32_t kMaskedOffset = 0x80000000u;
+
+template <int32_t POLICY, class T>
+__device__ __forceinline__ void store_buffer(__amdgpu_buffer_rsrc_t r, uint32_t off, T v) {
+  if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_plain, v), r, off, 0, POLICY);
+  else if constexpr (sizeof(T) == 8) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_plain, v), r, off, 0, POLICY);
+  else if constexpr (sizeof(T) == 4) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, POLICY);
+  else if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, POLICY);
+  else __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(uint8_t, v), r, off, 0, POLICY);
+}
+
+// An empty asm statement that uses the first word of a loaded value: the load
+// stays where it is issued (ahead of the guarded stores that follow) instead
+// of being moved under its own store's guard.
+template <class T>
+__device__ __forceinline__ void keep_load_ahead(const T& x) {
+  if constexpr (sizeof(T) >= 4) {
+    uint32_t w;
+    __builtin_memcpy(&w, &x, 4);
+    asm volatile("" ::"v"(w));
+  } else {
+    asm volatile("" ::"v"(static_cast<uint32_t>(x)));
+  }
 }
 
 template <int BYTES> struct VecOf;
@@ -687,22 +726,28 @@ __device__ __forceinline__ void load_batch(const GatherParams& p, const PageSrc&
   for (int u = 0; u < unroll_of<SH, M>(); ++u) M::load(p, s, min(c0 + u * SH::threads, n - 1), r[u]);
 }
 
-// Stores of one batch.  Each store is guarded by its own lane's bound, except
-// on flat pages with the wide shape: there a wave whose lanes all have their
-// first U - 1 chunks in range (every wave of a full page: a page's chunk count
-// is a multiple of 64, so the wave's lanes agree on each chunk but the last)
-// waits for all its loads, converts every chunk, and issues those U - 1
-// stores back to back, then the last one under its lane guard; and 16-byte
-// fp8 chunks of such pages go out as device-scope (write-through) streaming
-// stores.  Both were measured: they shorten the 300K fp8 gather by 4% and the
-// skew-8 raw one by 1.5%, and slow the narrow-shape and strided gathers down,
-// which keep the guarded stores.
+// Stores of one batch.  Each chunk past the unit's end is masked: by an
+// out-of-range buffer offset (flat pages that convert or take the wide shape,
+// no branch) or by its lane's guard (the rest).  On flat pages with the wide
+// shape, a wave whose lanes all have their first U - 1 chunks in range (every
+// wave of a full page: a page's chunk count is a multiple of 64, so the
+// wave's lanes agree on each chunk but the last) waits for all its loads,
+// converts every chunk, and issues those U - 1 stores back to back, then the
+// last one masked; and 16-byte fp8 chunks of such pages go out as
+// device-scope (write-through) streaming stores.  Both were measured: they
+// shorten the 300K fp8 gather by 4% and the skew-8 raw one by 1.5%, and slow
+// the narrow-shape and strided gathers down.
 template <class SH, class M>
 __device__ __forceinline__ void store_batch(const GatherParams& p, const PageDst& d, uint32_t n, uint32_t c0,
                                             const typename M::Reg (&r)[unroll_of<SH, M>()], float scale) {
   constexpr int U = unroll_of<SH, M>();
   constexpr bool burst = SH::threads == Wide::threads && M::layout == kFlat && U >= 2;
   constexpr bool write_through = burst && !M::is_copy && M::out_bytes == 16;
+  // masked buffer stores for flat pages that convert or take the wide shape; raw
+  // copies in the narrower shapes keep lane-guarded stores, where a batch's
+  // slots past the unit's end (a 9 KiB unit fills 2.25 of the small shape's 5)
+  // would otherwise all issue dropped stores
+  constexpr bool buffer_stores = M::layout == kFlat && (!M::is_copy || SH::threads == Wide::threads);
   if constexpr (burst) {
     // chunk c0 of the wave's last lane (wave-uniform): in range means every lane is
     const uint32_t wave_last = static_cast<uint32_t>(uniform(static_cast<int32_t>(c0 - (threadIdx.x & 63u)))) + 63u;
@@ -719,10 +764,20 @@ __device__ __forceinline__ void store_batch(const GatherParams& p, const PageDst
       return;
     }
   }
+  if constexpr (buffer_stores) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t c = c0 + u * SH::threads;
-    if (c < n) M::template store<write_through>(p, d, c, M::convert(r[u], scale));
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = c0 + u * SH::threads;
+      store_buffer<write_through ? kPolicyDeviceStream : kPolicyStream>(d.rsrc, c < n ? c * M::out_bytes : kMaskedOffset,
+                                                                        M::convert(r[u], scale));
+    }
+  } else {
+    if constexpr (M::layout == kFlat) keep_load_ahead(r[0]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = c0 + u * SH::threads;
+      if (c < n) M::template store<write_through>(p, d, c, M::convert(r[u], scale));
+    }
   }
 }
 

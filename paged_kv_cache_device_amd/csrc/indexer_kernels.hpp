@@ -115,12 +115,8 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
 }
 
 // 16-byte chunks are stored through a buffer resource over the wave's own
-// destination rows (fewer than 2^31 bytes: the host checks the row stride).
-// A masked chunk takes an offset past the resource's range, and the hardware
-// drops such a store, so the stores need no branch: without one the compiler
-// keeps every load ahead of the stores and waits for them one by one.
-constexpr uint32_t kIndexerMaskedOffset = 0x80000000u;
-constexpr int32_t kIndexerStorePolicy = 0x02;  // nt: streamed, as the nontemporal stores
+// destination rows (fewer than 2^31 bytes: the host checks the row stride),
+// masked chunks with an out-of-range offset (store_buffer): no branch.
 
 // Grid: any size; wave w of workgroup g takes rows from (g * 4 + w) * 64 on,
 // striding by the grid's rows.  Source rows are dword-aligned (the host checks
@@ -226,16 +222,12 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
         for (int k = 0; k < BATCH; ++k) {
           const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));
           const uint32_t o = take[k] ? (c / CPR) * static_cast<uint32_t>(p.dst_value_stride) + (c % CPR) * W
-                                     : kIndexerMaskedOffset;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_plain, v[k]), dst_rows, o, 0,
-                                                 kIndexerStorePolicy);
+                                     : kMaskedOffset;
+          store_buffer<kPolicyStream>(dst_rows, o, v[k]);
         }
       } else {
-        // A use of the first chunk keeps its load ahead of the masked stores:
-        // the compiler would otherwise move that load under its store's mask,
-        // after the other loads, and the first store would wait for every
-        // load instead of the first one.
-        asm volatile("" ::"v"(static_cast<uint32_t>(v[0])));
+        // lane-guarded stores: keep the first chunk's load ahead of them
+        keep_load_ahead(v[0]);
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
           const uint32_t c = static_cast<uint32_t>(lane + 64 * (k0 + k));

@@ -232,3 +232,26 @@ def test_indexer_graph_replays():
         assert torch.equal(got_v.cpu(), want_v), f"replay {rep}: values differ"
         assert torch.equal(got_s.cpu().view(torch.uint8), want_s.view(torch.uint8)), \
             f"replay {rep}: scales differ"
+
+
+@pytest.mark.parametrize("pitch", [(1 << 25) - 16, 1 << 25])
+def test_indexer_destination_pitch_at_the_store_range(pitch):
+    """16-byte chunks are stored through a resource over a wave's 64
+    destination rows, which must span fewer than 2^31 bytes: at a pitch just
+    under 32 MiB the 64 rows of the first wave span 2^31 - 1 KiB; at 32 MiB
+    the host takes byte chunks instead.  Rows 0..63 fill the first wave (two
+    batches), row 64 (padding) the second.  The gathered columns match the
+    oracle and every byte past them stays untouched."""
+    hd = 128
+    iw = workloads.make_indexer_workload(f"ix_pitch_{pitch}", [40, 24], 16, hd, 8, seed=pitch % 997,
+                                         pad_rows=1, value_cols=pitch)
+    log(f"[indexer parity] destination pitch {pitch}: T={iw.num_tokens} bytes={iw.num_tokens * pitch}")
+    want_v, want_s, rows = oracle.run_indexer_workload(iw)
+    assert rows == 64
+    d = iw.to(DEV)
+    got_v, got_s = d.fresh_values(), d.fresh_scales()
+    run_indexer_hip(d, got_v, got_s)
+    torch.cuda.synchronize()
+    assert torch.equal(got_v[:, :hd].cpu(), want_v[:, :hd])
+    assert bool((got_v[:, hd:] == workloads.SENTINEL_BYTE).all())
+    assert torch.equal(got_s.cpu().view(torch.uint8), want_s.view(torch.uint8))
