@@ -24,6 +24,11 @@
 //    consecutive chunks, so one wave instruction covers 1 KiB of a row span;
 //    a whole page's loads are in flight before the matching stores, with the
 //    nontemporal cache policy (each byte is touched once);
+//  * flat pages that convert, or take the wide shape, store through a buffer
+//    resource over the page's output, and a chunk past the unit's end takes
+//    an offset beyond its range, which the hardware drops: the stores need no
+//    branch, so the compiler keeps each load ahead of them and each store
+//    waits only for its own load;
 //  * all addressing that can exceed 2^31 bytes (page bases, output row bases)
 //    is int64; in-page offsets are 32-bit (the host guarantees that a page's
 //    rows span < 2^31 bytes);
