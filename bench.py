@@ -207,17 +207,24 @@ def time_steps(sets, steps: int, warmup: int):
     return wall, e0.elapsed_time(e1)
 
 
-def cold_latency(wl_dev, reps: int, scrub_bytes: int = 1 << 30):
+def cold_latency(wl_dev, reps: int, scrub_bytes: int = 1 << 30, read_scrub: bool = False):
     """Median / p10 / p90 (us) of one call after scrubbing >= 1 GiB (4x the
-    Infinity Cache) with a fill kernel, bracketed by events on the launch stream."""
+    Infinity Cache), bracketed by events on the launch stream.  The scrub is a
+    fill kernel (the default), or with `read_scrub` a sum over the same bytes:
+    it evicts the call's data as well but leaves clean lines behind, so the
+    call does not also write back the scrub's dirty lines."""
     import torch
 
     dev = wl_dev.cache.device if hasattr(wl_dev, "cache") else wl_dev.workspace.device
     scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=dev)
+    scrub.fill_(1)
     run = call_for(wl_dev, getattr(wl_dev, "workspace", None))
     out = []
     for i in range(reps + 3):
-        scrub.fill_(i)
+        if read_scrub:
+            scrub.sum()
+        else:
+            scrub.fill_(i)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         run()
@@ -408,7 +415,9 @@ def measure(wl, dev, args) -> dict:
     warm_us = ev_w / args.steps * 1e3
     del sets
     cold = cold_latency(g, args.cold_reps)
-    log(f"[bench] {wl.name}: cold scrubbed median {cold['median_us']:.2f} us; warm {warm_us:.2f} us")
+    cold_read = cold_latency(g, args.cold_reps, read_scrub=True)
+    log(f"[bench] {wl.name}: cold scrubbed median {cold['median_us']:.2f} us (after a read scrub "
+        f"{cold_read['median_us']:.2f} us); warm {warm_us:.2f} us")
     torch.cuda.empty_cache()
     return {
         "value": round(achieved, 2),
@@ -423,6 +432,7 @@ def measure(wl, dev, args) -> dict:
         "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
         "per_launch_us": round(kern_ms * 1e3, 3),
         "latency_us": {"cold_scrubbed_single_call": {k: round(v, 3) for k, v in cold.items()},
+                       "cold_read_scrubbed_single_call": {k: round(v, 3) for k, v in cold_read.items()},
                        "back_to_back_per_launch_cold": round(kern_ms * 1e3, 3),
                        "back_to_back_per_launch_warm": round(warm_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
