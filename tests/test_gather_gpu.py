@@ -177,6 +177,36 @@ def test_wide_shape_random(seed):
     check_parity(wl, DEV)
 
 
+WIDE_NARROW = [
+    # (cache dtype, entry, block size, pages, chunk bytes): raw pages of more than 36 KiB, at
+    # least 1,024 of them, in a batch of 4 requests with a sparse table (not walked)
+    (torch.bfloat16, 12, 2048, 1100, 8),   # 24-byte rows, 48 KiB pages
+    (torch.bfloat16, 6, 8192, 1030, 4),    # 12-byte rows, 96 KiB pages in two parts
+    (torch.bfloat16, 7, 4096, 1030, 2),    # 14-byte rows, 56 KiB pages
+    (torch.uint8, 577, 128, 1100, 1),      # 577-byte rows, 72 KiB pages in two parts
+]
+
+
+@pytest.mark.parametrize("dtype,entry,bs,pages,width", WIDE_NARROW)
+def test_wide_shape_narrow_chunks(dtype, entry, bs, pages, width):
+    """The wide shape with 8-, 4-, 2- and 1-byte raw chunks: its store bursts
+    on whole waves and, on the waves a ragged page leaves partly filled,
+    buffer stores whose chunks past the page's end take an out-of-range
+    offset.  Ragged lengths and seq_starts give partial first and last pages."""
+    R = 4
+    per = pages // R
+    lens = [per * bs - 5, per * bs + bs // 3, per * bs - bs // 2 + 1, per * bs + 7]
+    starts = [3, 0, bs // 2 + 1, 1]
+    need = [-(-n // bs) for n in lens]
+    wl = workloads.make_workload(f"wide_narrow_{entry}_{bs}", workloads.RAW, lens, bs, entry,
+                                 sum(need) + 8, seed=entry + bs, starts=starts,
+                                 width=2 * max(need) + 3, cache_dtype=dtype)
+    plan = plan_of(wl.to(DEV))
+    log(f"[wide narrow] entry={entry} bs={bs} T={wl.num_tokens} plan={plan}")
+    assert (plan["threads"], plan["access_width"], plan["flat"]) == (1024, width, 1), plan
+    check_parity(wl, DEV)
+
+
 @pytest.mark.parametrize("bs,lens,kind", [
     (1024, [20000], workloads.RAW),
     (1024, [20000], workloads.UPCONVERT),
