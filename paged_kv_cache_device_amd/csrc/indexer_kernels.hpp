@@ -128,8 +128,28 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
 // a branch, and only the stores are masked.  W == 16 needs dword-aligned
 // destination rows and 64 * dst_value_stride < 2^31 (the host picks W == 1
 // otherwise).  Dynamic LDS (kCuLds): (num_batches + 1) int32.
+//
+// The fields the first two dependent loads need (batch ids, batch extents,
+// their counts, the block table and its geometry) are leading scalar
+// arguments, preloaded into SGPRs at wave start; read from the parameter
+// struct instead, each wave would first wait for two scalar-load round trips
+// before its first batch-id load could leave.  The struct's copies of those
+// fields are ignored.
 template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W, int CU>
-__global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(IndexerParams p) {
+__global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(
+    const int32_t* token_to_seq, const int32_t* cu_seqlen, int32_t num_tokens, int32_t num_batches,
+    const int32_t* block_table, int64_t block_table_ld, int32_t block_table_width, int32_t block_size,
+    uint32_t block_size_magic, IndexerParams params) {
+  IndexerParams p = params;
+  p.token_to_seq = token_to_seq;
+  p.cu_seqlen = cu_seqlen;
+  p.num_tokens = num_tokens;
+  p.num_batches = num_batches;
+  p.block_table = block_table;
+  p.block_table_ld = block_table_ld;
+  p.block_table_width = block_table_width;
+  p.block_size = block_size;
+  p.block_size_magic = block_size_magic;
   using V = typename IndexerChunk<W>::T;
   constexpr int CPR = HEAD_DIM / W;  // chunks per row
   constexpr int WAVES = kIndexerThreads / 64;
@@ -144,10 +164,15 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
   const int lane = threadIdx.x & 63;
   // wave-uniform, so a wave's row range and its destination resource sit in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t stride_rows = int64_t(gridDim.x) * WAVES * kIndexerRowsPerWave;
+  const int64_t first_row0 = (int64_t(blockIdx.x) * WAVES + wave) * kIndexerRowsPerWave;
+  if (first_row0 >= p.num_tokens) return;
   const int32_t ncu = p.num_batches + 1;
 
-  // the batch extents, requested before the first rows' batch ids are needed
+  // The first rows' batch ids and the batch extents leave first thing, from
+  // preloaded arguments only: the loop below needs fields of the parameter
+  // struct, and the compiler waits for their scalar loads before its body.
+  const int32_t first_row = static_cast<int32_t>(first_row0) + lane;
+  const int32_t first_batch = p.token_to_seq[first_row < p.num_tokens ? first_row : p.num_tokens - 1];
   int32_t cu_lane = 0;
   if constexpr (CU == kCuWave) {
     cu_lane = p.cu_seqlen[lane < ncu ? lane : ncu - 1];
@@ -155,13 +180,13 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(Indexer
     for (int i = threadIdx.x; i < ncu; i += kIndexerThreads) cu_lds[i] = p.cu_seqlen[i];
     __syncthreads();
   }
+  const int64_t stride_rows = int64_t(gridDim.x) * WAVES * kIndexerRowsPerWave;
 
-  for (int64_t row0 = (int64_t(blockIdx.x) * WAVES + wave) * kIndexerRowsPerWave; row0 < p.num_tokens;
-       row0 += stride_rows) {
+  for (int64_t row0 = first_row0; row0 < p.num_tokens; row0 += stride_rows) {
     // --- this lane's row: its batch, position, block and source ------------
     const int32_t row = static_cast<int32_t>(row0) + lane;
     bool ok = row < p.num_tokens;
-    const int32_t batch = p.token_to_seq[ok ? row : p.num_tokens - 1];
+    const int32_t batch = row0 == first_row0 ? first_batch : p.token_to_seq[ok ? row : p.num_tokens - 1];
     ok = ok && batch >= 0 && batch < p.num_batches;
     const int32_t b = ok ? batch : 0;
     int32_t start, end;

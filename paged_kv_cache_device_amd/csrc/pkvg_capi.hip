@@ -664,14 +664,14 @@ bool indexer_structure_supported(int32_t layout, int32_t head_dim, int32_t block
 template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W>
 hipError_t launch_indexer_cu(const pkvg::IndexerParams& p, unsigned grid, hipStream_t stream) {
   const int32_t ncu = p.num_batches + 1;
-  if (ncu <= 64)
-    return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuWave>, grid,
-                  pkvg::kIndexerThreads, 0, stream, p);
-  if (ncu <= pkvg::kIndexerLdsCuMax)
-    return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuLds>, grid,
-                  pkvg::kIndexerThreads, sizeof(int32_t) * size_t(ncu), stream, p);
-  return launch(pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuGlobal>, grid,
-                pkvg::kIndexerThreads, 0, stream, p);
+  const int cu = ncu <= 64 ? pkvg::kCuWave : (ncu <= pkvg::kIndexerLdsCuMax ? pkvg::kCuLds : pkvg::kCuGlobal);
+  const size_t lds = cu == pkvg::kCuLds ? sizeof(int32_t) * size_t(ncu) : 0;
+  auto kernel = cu == pkvg::kCuWave  ? pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuWave>
+                : cu == pkvg::kCuLds ? pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuLds>
+                                     : pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuGlobal>;
+  return launch(kernel, grid, pkvg::kIndexerThreads, lds, stream, p.token_to_seq, p.cu_seqlen, p.num_tokens,
+                p.num_batches, p.block_table, p.block_table_ld, p.block_table_width, p.block_size,
+                p.block_size_magic, p);
 }
 
 template <int LAYOUT, int HEAD_DIM, int BT, int HT>
