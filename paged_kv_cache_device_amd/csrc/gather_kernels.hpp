@@ -738,16 +738,22 @@ __device__ __forceinline__ void load_batch(const GatherParams& p, const PageSrc&
 // wave of a full page: a page's chunk count is a multiple of 64, so the
 // wave's lanes agree on each chunk but the last) waits for all its loads,
 // converts every chunk, and issues those U - 1 stores back to back, then the
-// last one masked; and 16-byte fp8 chunks of such pages go out as
-// device-scope (write-through) streaming stores.  Both were measured: they
-// shorten the 300K fp8 gather by 4% and the skew-8 raw one by 1.5%, and slow
-// the narrow-shape and strided gathers down.
+// last one masked (the 300K fp8 gather -4%, skew-8 raw -1.5%; slower on the
+// narrow-shape and strided gathers).  16-byte chunks of flat pages go out as
+// device-scope (write-through) streaming stores, raw copies in every shape
+// and fp8 pages in the wide shape: nothing is left dirty in the XCD's L2 for
+// the end of the launch to write back (a single cold call of the 60K raw
+// gather 28.1 -> 27.1 us, back to back 24.83 -> 24.67 us).  Row-layout pages
+// keep nontemporal stores: their rows' partial lines would reach memory as
+// separate masked writes.
 template <class SH, class M>
 __device__ __forceinline__ void store_batch(const GatherParams& p, const PageDst& d, uint32_t n, uint32_t c0,
                                             const typename M::Reg (&r)[unroll_of<SH, M>()], float scale) {
   constexpr int U = unroll_of<SH, M>();
   constexpr bool burst = SH::threads == Wide::threads && M::layout == kFlat && U >= 2;
-  constexpr bool write_through = burst && !M::is_copy && M::out_bytes == 16;
+  // device-scope write-through stores for 16-byte chunks of flat pages: raw
+  // copies in every shape, fp8 pages in the wide shape
+  constexpr bool write_through = M::layout == kFlat && M::out_bytes == 16 && (burst || M::is_copy);
   // masked buffer stores for flat pages that convert or take the wide shape; raw
   // copies in the narrower shapes keep lane-guarded stores, where a batch's
   // slots past the unit's end (a 9 KiB unit fills 2.25 of the small shape's 5)
@@ -1110,6 +1116,9 @@ __device__ __forceinline__ void move_group(const GatherParams& p, int32_t lane_p
   constexpr int U = unroll_of<SH, M>();
   const uint32_t cpr = static_cast<uint32_t>(p.chunks_per_row);
   const uint32_t bs = static_cast<uint32_t>(p.page_tokens);
+  // a flat group's output: n chunks from dst_first (fewer than 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t group_out =
+      __builtin_amdgcn_make_buffer_rsrc(dst_first, 0, static_cast<int32_t>(n * M::out_bytes), kBufferWord3);
   for (uint32_t c0 = threadIdx.x; c0 - threadIdx.x < n; c0 += SH::threads * U) {
     uint32_t row[U], col[U], k[U];
 #pragma unroll
@@ -1134,6 +1143,11 @@ __device__ __forceinline__ void move_group(const GatherParams& p, int32_t lane_p
     for (int u = 0; u < U; ++u) {
       const uint32_t c = c0 + u * SH::threads;
       if (phys[u] < 0 || c >= n) continue;
+      if constexpr (LAYOUT == kFlat && M::out_bytes == 16) {
+        // device-scope write-through, as the page kernel's flat 16-byte chunks
+        store_write_through(group_out, c * M::out_bytes, __builtin_bit_cast(u32x4_plain, M::convert(r[u], scale)));
+        continue;
+      }
       uint8_t* q;
       if constexpr (LAYOUT == kFlat) {
         q = dst_first + c * M::out_bytes;
