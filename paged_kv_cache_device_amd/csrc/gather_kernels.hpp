@@ -740,20 +740,18 @@ __device__ __forceinline__ void load_batch(const GatherParams& p, const PageSrc&
 // converts every chunk, and issues those U - 1 stores back to back, then the
 // last one masked (the 300K fp8 gather -4%, skew-8 raw -1.5%; slower on the
 // narrow-shape and strided gathers).  16-byte chunks of flat pages go out as
-// device-scope (write-through) streaming stores, raw copies in every shape
-// and fp8 pages in the wide shape: nothing is left dirty in the XCD's L2 for
-// the end of the launch to write back (a single cold call of the 60K raw
-// gather 28.1 -> 27.1 us, back to back 24.83 -> 24.67 us).  Row-layout pages
-// keep nontemporal stores: their rows' partial lines would reach memory as
-// separate masked writes.
+// device-scope (write-through) streaming stores, in every shape: nothing is
+// left dirty in the XCD's L2 for the end of the launch to write back (a
+// single cold call of the 60K raw gather 28.1 -> 27.1 us, back to back
+// 24.83 -> 24.67 us).  Row-layout pages keep nontemporal stores: their rows'
+// partial lines would reach memory as separate masked writes.
 template <class SH, class M>
 __device__ __forceinline__ void store_batch(const GatherParams& p, const PageDst& d, uint32_t n, uint32_t c0,
                                             const typename M::Reg (&r)[unroll_of<SH, M>()], float scale) {
   constexpr int U = unroll_of<SH, M>();
   constexpr bool burst = SH::threads == Wide::threads && M::layout == kFlat && U >= 2;
-  // device-scope write-through stores for 16-byte chunks of flat pages: raw
-  // copies in every shape, fp8 pages in the wide shape
-  constexpr bool write_through = M::layout == kFlat && M::out_bytes == 16 && (burst || M::is_copy);
+  // device-scope write-through stores for every 16-byte chunk of a flat page
+  constexpr bool write_through = M::layout == kFlat && M::out_bytes == 16;
   // masked buffer stores for flat pages that convert or take the wide shape; raw
   // copies in the narrower shapes keep lane-guarded stores, where a batch's
   // slots past the unit's end (a 9 KiB unit fills 2.25 of the small shape's 5)
