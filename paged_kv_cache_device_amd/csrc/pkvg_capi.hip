@@ -40,9 +40,10 @@ static_assert(pkvg::kWaveRegs == PKVG_TASKS_WAVE && pkvg::kLdsPrefix == PKVG_TAS
 
 thread_local int g_last_hip_error = 0;
 
-// Workgroups launched: one per task up to this cap; any grid is correct
-// because workgroups stride over tasks.
-constexpr int64_t kMaxGrid = int64_t(1) << 20;
+// Workgroups launched: one per task up to this cap (32 times the workgroups
+// the chip holds at once); any grid is correct because workgroups stride over
+// tasks, and beyond the cap they do.
+constexpr int64_t kMaxGrid = int64_t(1) << 16;
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -691,8 +692,9 @@ hipError_t launch_indexer_dim(const pkvg::IndexerParams& p, int32_t head_dim, bo
 }
 
 // Rows per workgroup (four waves of 64 rows); the grid covers every row once,
-// up to this many workgroups (more rows are taken by striding).
-constexpr int64_t kIndexerMaxGrid = int64_t(1) << 20;
+// up to this many workgroups (8 times what the chip holds at once; more rows,
+// past 4,194,304, are taken by striding).
+constexpr int64_t kIndexerMaxGrid = int64_t(1) << 14;
 
 // Validates an indexer gather and fills its parameters; touches no device.
 int prepare_indexer(const void* cache, int64_t num_blocks, int32_t block_size, int64_t block_stride,

@@ -207,6 +207,28 @@ def test_wide_shape_narrow_chunks(dtype, entry, bs, pages, width):
     check_parity(wl, DEV)
 
 
+@pytest.mark.parametrize("case", ["pages", "one_token_groups"])
+def test_tasks_beyond_the_grid(case):
+    """More task units than the launch has workgroups (the grid is capped at
+    65,536): workgroups stride over the tasks, and every task after a
+    workgroup's first looks its block-table entries up inside the loop
+    instead of taking the ones fetched with the request extent.  One request
+    of 614,400 tokens in 9 KiB units (76,798 units) and one of 600,000
+    one-token pages in 8-page groups (75,002 groups), with seq_starts; the
+    whole workspace against the oracle."""
+    if case == "pages":
+        wl = workloads.make_workload("grid_cap_pages", workloads.RAW, [614400], 64, 576,
+                                     614400 // 64 + 9, seed=71, starts=[37])
+    else:
+        wl = workloads.make_workload("grid_cap_groups", workloads.RAW, [600000], 1, 576, 600017,
+                                     seed=73, starts=[5])
+    plan = plan_of(wl.to(DEV))
+    log(f"[grid cap] {case}: T={wl.num_tokens} plan={plan}")
+    assert plan["task_mode"] == pkvg.PKVG_TASKS_SINGLE
+    assert plan["grid"] < plan["task_capacity"], plan
+    check_parity(wl, DEV)
+
+
 @pytest.mark.parametrize("bs,lens,kind", [
     (1024, [20000], workloads.RAW),
     (1024, [20000], workloads.UPCONVERT),

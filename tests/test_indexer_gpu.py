@@ -255,3 +255,15 @@ def test_indexer_destination_pitch_at_the_store_range(pitch):
     assert torch.equal(got_v[:, :hd].cpu(), want_v[:, :hd])
     assert bool((got_v[:, hd:] == workloads.SENTINEL_BYTE).all())
     assert torch.equal(got_s.cpu().view(torch.uint8), want_s.view(torch.uint8))
+
+
+def test_indexer_rows_beyond_the_grid():
+    """More rows than one pass of the capped grid covers (16,384 workgroups of
+    256 rows = 4,194,304 rows): waves stride to their next 64 rows and load
+    those rows' batch ids inside the loop.  One sequence of 4,300,000 tokens
+    and padding rows past it."""
+    n = 4_300_000
+    iw = workloads.make_indexer_workload("ix_grid_cap", [n], 64, 128, -(-n // 64) + 5, seed=81,
+                                         pad_rows=70)
+    assert iw.num_tokens > 16384 * 256
+    check_indexer_parity(iw)
