@@ -74,6 +74,7 @@ enum IndexerCuSource : int {
   kCuGlobal = 2,  // larger: each row loads its two entries after its batch id
 };
 constexpr int kIndexerLdsCuMax = 4096;
+static_assert(kIndexerLdsCuMax % kIndexerThreads == 0, "whole rounds of a workgroup's loads");
 
 // Byte offset of chunk j (bytes j*W .. j*W+W-1 of a token) from the token's
 // first value byte (indexer_row_base): consecutive in the flat layout; in the
@@ -168,19 +169,33 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(
   // wave-uniform, so a wave's row range and its destination resource sit in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t first_row0 = (int64_t(blockIdx.x) * WAVES + wave) * kIndexerRowsPerWave;
-  if (first_row0 >= p.num_tokens) return;
   const int32_t ncu = p.num_batches + 1;
 
   // The first rows' batch ids and the batch extents leave first thing, from
   // preloaded arguments only: the loop below needs fields of the parameter
   // struct, and the compiler waits for their scalar loads before its body.
+  // Every wave gets here (a wave past the last row reads row num_tokens - 1
+  // and skips the loop), so all of a workgroup's waves reach the barrier.
   const int32_t first_row = static_cast<int32_t>(first_row0) + lane;
   const int32_t first_batch = p.token_to_seq[first_row < p.num_tokens ? first_row : p.num_tokens - 1];
   int32_t cu_lane = 0;
   if constexpr (CU == kCuWave) {
     cu_lane = p.cu_seqlen[lane < ncu ? lane : ncu - 1];
   } else if constexpr (CU == kCuLds) {
-    for (int i = threadIdx.x; i < ncu; i += kIndexerThreads) cu_lds[i] = p.cu_seqlen[i];
+    // at most 16 entries per thread, all requested before any is written (a
+    // load-then-store loop would wait for each in turn)
+    constexpr int kPer = kIndexerLdsCuMax / kIndexerThreads;
+    int32_t e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = static_cast<int>(threadIdx.x) + k * kIndexerThreads;
+      e[k] = p.cu_seqlen[i < ncu ? i : ncu - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = static_cast<int>(threadIdx.x) + k * kIndexerThreads;
+      if (i < ncu) cu_lds[i] = e[k];
+    }
     __syncthreads();
   }
   const int64_t stride_rows = int64_t(gridDim.x) * WAVES * kIndexerRowsPerWave;
