@@ -1262,25 +1262,69 @@ __global__ __launch_bounds__(SH::threads) void gather_groups_kernel(
 // ---------------------------------------------------------------------------
 
 // One workgroup of kScanThreads: P[0..R] = exclusive prefix of page counts,
-// *count = P[R].
+// *count = P[R].  A round covers kScanPer * kScanThreads requests.  Their
+// extents and starts are loaded in coalesced slices (lane t of slice k on
+// request base + k * kScanThreads + t), all requested, at clamped indices,
+// before any is used; the page counts go through LDS so that each thread
+// takes kScanPer consecutive requests, sums them, and one block scan orders
+// the round; the prefixes go back through LDS and out in coalesced slices.
+// One memory round trip and one block scan per round, where a round of one
+// slice cost both per kScanThreads requests (60,000 requests 56.5 us).
+constexpr int kScanPer = 8;
+
 __global__ __launch_bounds__(kScanThreads) void scan_page_counts_kernel(GatherParams p, int32_t* P,
                                                                         int32_t* count) {
   __shared__ int32_t scan_tmp[kScanThreads / 64];
+  __shared__ int32_t round_lds[kScanPer * kScanThreads];  // the round's counts, then its prefixes
   const int32_t R = p.num_reqs;
+  const int32_t ncu = R + p.cu_terminal;  // cu_seq_lens entries
+  const int32_t t = static_cast<int32_t>(threadIdx.x);
   int32_t carry = 0;
-  for (int32_t base = 0; base < R; base += kScanThreads) {
-    const int32_t r = base + static_cast<int32_t>(threadIdx.x);
-    int32_t c = 0;
-    if (r < R) {
-      const int64_t b = clamp_rows(p.cu_seq_lens[r], p.num_tokens);
-      const int64_t e = clamp_rows(request_end(p, r), p.num_tokens);
-      const int32_t s = p.seq_starts ? p.seq_starts[r] : 0;
-      c = page_count(p, b, e, s);
+  for (int32_t base = 0; base < R; base += kScanThreads * kScanPer) {
+    int32_t cb[kScanPer], ce[kScanPer], st[kScanPer];
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int32_t r = base + k * kScanThreads + t;
+      cb[k] = p.cu_seq_lens[min(r, ncu - 1)];
+      ce[k] = p.cu_seq_lens[min(r + 1, ncu - 1)];
+      st[k] = p.seq_starts ? p.seq_starts[min(r, R - 1)] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int32_t r = base + k * kScanThreads + t;
+      int32_t c = 0;
+      if (r < R) {
+        // request_end: the next entry, or num_tokens for the last request
+        // when cu_seq_lens has no terminal entry
+        const int64_t e_raw = (p.cu_terminal || r + 1 < R) ? ce[k] : p.num_tokens;
+        c = page_count(p, clamp_rows(cb[k], p.num_tokens), clamp_rows(e_raw, p.num_tokens), st[k]);
+      }
+      round_lds[k * kScanThreads + t] = c;
+    }
+    __syncthreads();
+    // thread t: requests base + t * kScanPer .. + kScanPer - 1 (0 past R)
+    int32_t v[kScanPer];
+    int32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      v[j] = round_lds[t * kScanPer + j];
+      sum += v[j];
     }
     int32_t total;
-    const int32_t off = block_exclusive_scan<kScanThreads>(c, scan_tmp, total);
-    if (r < R) P[r] = carry + off;
+    int32_t off = carry + block_exclusive_scan<kScanThreads>(sum, scan_tmp, total);  // ends with a barrier
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      round_lds[t * kScanPer + j] = off;
+      off += v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int32_t r = base + k * kScanThreads + t;
+      if (r < R) P[r] = round_lds[k * kScanThreads + t];
+    }
     carry += total;
+    __syncthreads();  // the next round rewrites round_lds
   }
   if (threadIdx.x == 0) {
     P[R] = carry;
