@@ -430,6 +430,10 @@ def measure(wl, dev, args) -> dict:
         "config": workload_config(wl, alg_bytes),
         "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
         "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
+        # the same algorithmic bytes over the cold single call's median (one launch from an idle
+        # GPU, timed alone: it carries the launch's own fixed cost)
+        "cold_single_call_gbs": round(alg_bytes / (cold["median_us"] * 1e-6) / 1e9, 2),
+        "cold_single_call_pct_of_peak": round(100.0 * alg_bytes / (cold["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "per_launch_us": round(kern_ms * 1e3, 3),
         "latency_us": {"cold_scrubbed_single_call": {k: round(v, 3) for k, v in cold.items()},
                        "cold_read_scrubbed_single_call": {k: round(v, 3) for k, v in cold_read.items()},
@@ -582,6 +586,8 @@ def main():
         "pct_of_peak": head["pct_of_peak"],
         "wall_ms_per_step": head["wall_ms_per_step"],
         "median_latency_us_cold_scrubbed": head["median_latency_us_cold_scrubbed"],
+        "cold_single_call_gbs": head["cold_single_call_gbs"],
+        "cold_single_call_pct_of_peak": head["cold_single_call_pct_of_peak"],
         "per_launch_us": head["per_launch_us"],
         "latency_us": head["latency_us"],
         "roofline": head["roofline"],
