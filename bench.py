@@ -17,8 +17,11 @@ enqueues the first calls, so the events see the calls back to back.
 `wall_ms_per_step` is the host clock over the same bracket, which adds the two
 synchronisation latencies and the spin.  The timed steps rotate over several copies of the
 inputs and outputs whose total is far above the 256 MB Infinity Cache, so no
-step finds its data in a cache.  Printed on stdout: ONE JSON line.  Progress
-goes to stderr.
+step finds its data in a cache.  Each workload also reports one cold call's
+latency (median, p10, p90 of 100: a 1 GiB fill or read, then events around one
+call) and the GB/s at that median; a single call from an idle GPU carries the
+launch's own fixed cost (an empty kernel takes about 6 us that way).  Printed
+on stdout: ONE JSON line.  Progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAME]
 """
