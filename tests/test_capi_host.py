@@ -199,3 +199,21 @@ def test_noalloc_rejects_batches_beyond_its_scratch(lib):
     assert lib.gather_maybe_dequant_noalloc(FAKE, 9, 100, 64, 576, 64 * 576, 576, FAKE, 10, 576,
                                             FAKE, 4, 4, FAKE, 1, None, 2000, None,
                                             None) == pkvg.PKVG_E_DTYPE
+
+
+def test_native_program_loads_without_a_gpu():
+    """The native C-ABI program links the library and the oracle through
+    relative run paths; where no GPU is visible it says so and exits 2
+    (no compute call is made)."""
+    import os
+    import subprocess
+
+    import torch
+
+    program = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "capi_native")
+    if not os.path.exists(program):
+        pytest.fail(f"{program} is not built: run __graft_entry__.build()")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the GPU test runs the program")
+    proc = subprocess.run([program], capture_output=True, text=True, timeout=60)
+    assert proc.returncode == 2 and "no GPU" in proc.stdout, proc.stdout + proc.stderr
