@@ -191,3 +191,69 @@ def test_plan_status_matches_the_call(bad):
     info = pkvg.PlanInfo()
     got = lib.pkvg_plan(RAW, a["kind"], *args, None, ctypes.byref(info))
     assert got == want != pkvg.PKVG_OK
+
+
+# --- property test: the host checks and the launch plan on random arguments ---
+
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+_STATUSES = {pkvg.PKVG_OK, pkvg.PKVG_E_NULL, pkvg.PKVG_E_SHAPE, pkvg.PKVG_E_STRIDE, pkvg.PKVG_E_DTYPE,
+             pkvg.PKVG_E_LIMIT}
+_POINTERS = [None, F, F + 1, F + 2, F + 4, F + 8]
+
+
+@settings(max_examples=400, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(data=st.data())
+def test_plan_on_random_arguments(data):
+    """pkvg_plan runs the calls' own checks and launch planning without touching
+    a device: on any arguments it returns one of the documented statuses, and
+    every plan it accepts respects the launch rules (grid cap, walked grids,
+    shapes, access widths, unit sizes).  Fake addresses are never read."""
+    draw = data.draw
+
+    def mostly(valid, odd):
+        # a valid value seven times in eight, else one from the edges
+        return draw(valid if draw(st.integers(0, 7)) else odd)
+
+    op = draw(st.sampled_from([RAW, DEQ, UP]))
+    kinds = {RAW: [1, 2, 4, 8], DEQ: [0, 1], UP: [0]}
+    kind = mostly(st.sampled_from(kinds[op]), st.sampled_from([-1, 0, 3, 9, 16]))
+    bs = mostly(st.sampled_from([1, 2, 3, 4, 8, 16, 32, 64, 128, 1024]),
+                st.one_of(st.integers(-2, 70), st.sampled_from([1 << 16, 1 << 20])))
+    entry = mostly(st.integers(1, 1200), st.sampled_from([-2, 0, 4096, 1 << 20]))
+    pad_c = draw(st.integers(0, 9))
+    sts = mostly(st.just(entry + pad_c), st.integers(-3, 1 << 34))
+    sbs = mostly(st.just(max(bs, 0) * (entry + pad_c)), st.integers(-3, 1 << 40))
+    drs = mostly(st.just(entry + draw(st.integers(0, 9))), st.integers(-3, 1 << 34))
+    T = mostly(st.integers(0, 400000), st.sampled_from([-2, -1, (1 << 31) - 1, (1 << 31) + 5, 1 << 40]))
+    R = mostly(st.one_of(st.integers(0, 80), st.integers(1000, 70000)), st.sampled_from([-2, -1, 1 << 20]))
+    width = mostly(st.integers(1, 5000), st.sampled_from([-2, 0, 1 << 20]))
+    ld = width + mostly(st.just(0), st.integers(-3, 64))
+    nb = mostly(st.integers(1, 1 << 20), st.sampled_from([-2, 0, 1 << 40]))
+    term = mostly(st.just(1), st.sampled_from([0, 2]))
+    ptr = lambda: mostly(st.just(F), st.sampled_from(_POINTERS))  # noqa: E731
+    src, dst, table, cu, starts, scale = ptr(), ptr(), ptr(), ptr(), ptr(), ptr()
+
+    info = pkvg.PlanInfo()
+    status = pkvg.library().pkvg_plan(op, kind, src, nb, bs, entry, sbs, sts, dst, T, drs, table, width,
+                                      ld, cu, term, starts, R, scale, ctypes.byref(info))
+    assert status in _STATUSES, status
+    if status != pkvg.PKVG_OK:
+        return
+    p = info.as_dict()
+    if p["grid"] == 0:  # no work: nothing is planned
+        assert all(v == 0 for v in p.values()), p
+        return
+    assert p["kernel"] in (pkvg.PKVG_KERNEL_PAGES, pkvg.PKVG_KERNEL_GROUPS), p
+    assert p["threads"] in (256, 1024) and p["access_width"] in (1, 2, 4, 8, 16), p
+    assert 1 <= p["grid"] <= 1 << 16, p
+    if p["task_mode"] == pkvg.PKVG_TASKS_WALK:
+        assert p["grid_rows"] == R and 1 <= R <= 65535, p
+    else:
+        assert p["grid_rows"] == 1 and p["grid"] == min(p["task_capacity"], 1 << 16), p
+    assert 0 <= p["group_shift"] <= 6 and p["split_shift"] >= 0, p
+    if p["group_shift"] > 0:
+        assert p["kernel"] == pkvg.PKVG_KERNEL_GROUPS and p["task_tokens"] == bs << p["group_shift"], p
+    else:
+        assert p["kernel"] == pkvg.PKVG_KERNEL_PAGES, p
+        assert p["task_tokens"] << p["split_shift"] == bs, p
