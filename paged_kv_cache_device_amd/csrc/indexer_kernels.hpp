@@ -23,7 +23,8 @@
 // Design for gfx950: the work unit is the output row (token_to_seq may send
 // any row to any batch, and padding rows carry -1), so a wave owns 64
 // consecutive rows.  Lane r resolves row r (token_to_seq, the batch's extent,
-// the block-table entry: three dependent loads) to a source address; then
+// the block-table entry: dependent loads, the entry of a row of the first
+// batch requested ahead, speculatively) to a source address; then
 // the wave moves the 64 rows' value bytes in W-byte chunks, consecutive lanes
 // on consecutive chunks of consecutive rows (a 16-byte chunk per lane puts
 // 1 KiB of contiguous rows under one wave instruction), taking each row's
@@ -126,10 +127,11 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
 // striding by the grid's rows.  Source rows are dword-aligned (the host checks
 // the cache base and the record stride; value rows start at multiples of 16
 // bytes inside a record), so bit 0 of a row's offset carries its mask when
-// the offset crosses lanes.  The host launches only with num_blocks >= 1 and
-// block_table_width >= 1 (otherwise every row is masked): a masked row keeps
-// an offset inside record 0, so every load is in bounds and goes out without
-// a branch, and only the stores are masked.  W == 16 needs dword-aligned
+// the offset crosses lanes.  The host launches only with num_tokens,
+// num_batches, num_blocks and block_table_width all >= 1 (otherwise every row
+// is masked): a masked row keeps an offset inside record 0, and the
+// speculative table entry lies in row 0 below the width, so every load is in
+// bounds and goes out without a branch, and only the stores are masked.  W == 16 needs dword-aligned
 // destination rows and 64 * dst_value_stride < 2^31 (the host picks W == 1
 // otherwise).  Dynamic LDS (kCuLds): (num_batches + 1) int32.
 //
@@ -198,6 +200,15 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(
     }
     __syncthreads();
   }
+  // A speculative block-table entry, requested with the batch ids: row 0's
+  // column first_row / block_size, the column of a row of batch 0 when
+  // cu_seqlen[0] == 0.  A first-round row whose batch turns out to be 0 and
+  // whose column is that one would load this same entry, so it takes it
+  // instead; a wave whose rows all do skips the dependent table load (one
+  // memory round trip fewer for the first batch's rows).
+  const uint32_t spec_col = div_magic(static_cast<uint32_t>(min(first_row, p.num_tokens - 1)),
+                                      static_cast<uint32_t>(p.block_size), p.block_size_magic);
+  const int32_t spec_block = p.block_table[min(spec_col, static_cast<uint32_t>(p.block_table_width - 1))];
   const int64_t stride_rows = int64_t(gridDim.x) * WAVES * kIndexerRowsPerWave;
 
   for (int64_t row0 = first_row0; row0 < p.num_tokens; row0 += stride_rows) {
@@ -224,7 +235,10 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(
     const uint32_t slot = pos - col * static_cast<uint32_t>(p.block_size);
     ok = ok && col < static_cast<uint32_t>(p.block_table_width);
     int32_t block = -1;
-    if (ok) block = p.block_table[int64_t(b) * p.block_table_ld + col];
+    if (ok) {
+      const bool same_entry = row0 == first_row0 && b == 0 && col == spec_col;
+      block = same_entry ? spec_block : p.block_table[int64_t(b) * p.block_table_ld + col];
+    }
     ok = ok && block >= 0 && block < p.num_blocks;
     // clamped to block 0 when invalid, then widened: the record stride is large
     const IndexerCache cache = (IndexerCache)p.cache;  // an address-space cast: the cache is global memory

@@ -713,7 +713,8 @@ int prepare_indexer(const void* cache, int64_t num_blocks, int32_t block_size, i
       block_table_ld < block_table_width)
     return PKVG_E_STRIDE;
   // no row can pass the masks: nothing to enqueue (a launched kernel relies on
-  // record 0 existing, as the address masked rows keep)
+  // record 0 existing, as the address masked rows keep, and on row 0 of the
+  // table having a column, which its speculative entry reads)
   if (num_tokens == 0 || num_batches == 0 || num_blocks == 0 || block_table_width == 0) {
     *nothing = true;
     return PKVG_OK;
