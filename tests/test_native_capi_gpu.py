@@ -1,7 +1,10 @@
 """The C ABI from a native program (tests/native/capi_native.cpp): no Python
-or torch in the path, device memory from hipMalloc, one call of
-gather_cache, gather_upconvert_fp8 and gather_indexer_quant_cache, every
-output byte checked by the program against the C oracle."""
+or torch in the path, device memory from hipMalloc.  Every compute entry point
+is called: the four paged gathers (gather_cache, gather_upconvert_fp8,
+gather_maybe_dequant auto and fp8, and its no-allocation variant) on a small
+batch and on 1,500 short requests, gather_page_tasks and
+gather_indexer_quant_cache; the program checks every output byte against the
+C oracle."""
 import os
 import subprocess
 
