@@ -329,14 +329,16 @@ def gather_upconvert_fp8(src_cache: torch.Tensor, dst: torch.Tensor, block_table
 
 def prepare(entry_point: str, *args, **kwargs) -> PreparedCall:
     """Marshal the arguments of ``gather_cache`` / ``gather_maybe_dequant`` /
-    ``gather_upconvert_fp8`` once, on the current stream; returns a callable."""
+    ``gather_maybe_dequant_noalloc`` / ``gather_upconvert_fp8`` once, on the
+    current stream (the same arguments as the function of that name); returns
+    a callable that enqueues the call."""
     stream = None
     if entry_point == "gather_cache":
         return _prepare_cache(*args, **kwargs, stream=stream)
-    if entry_point == "gather_maybe_dequant":
+    if entry_point in ("gather_maybe_dequant", "gather_maybe_dequant_noalloc"):
         kwargs.setdefault("scale", None)
         kwargs.setdefault("seq_starts", None)
-        return _prepare_maybe_dequant(*args, **kwargs, stream=stream)
+        return _prepare_maybe_dequant(*args, **kwargs, stream=stream, entry_point=entry_point)
     if entry_point == "gather_upconvert_fp8":
         kwargs.setdefault("seq_starts", None)
         return _prepare_upconvert(*args, **kwargs, stream=stream)

@@ -68,6 +68,32 @@ def test_noalloc_matches_gather_maybe_dequant(first, second):
         assert not bool((want.view(torch.uint8) == workloads.SENTINEL_BYTE).all())
 
 
+def test_noalloc_prepared_call():
+    """The binding's prepare() of the no-allocation entry point: marshalled once,
+    issued twice on a 2,000-request batch with another batch's no-allocation call
+    between them (which leaves its own task table in the shared scratch); each
+    issue matches gather_maybe_dequant byte for byte."""
+    wl = batch(2000, 9100, workloads.DEQUANT_FP8)
+    other = batch(1200, 9101, workloads.DEQUANT_AUTO)
+    d, o = wl.to(DEV), other.to(DEV)
+    want = d.fresh_workspace()
+    pkvg.gather_maybe_dequant(d.src_cache(), want[: d.num_tokens, : d.entry], d.block_table,
+                              d.cu_seq_lens, d.num_reqs, "fp8", d.scale_tensor, d.seq_starts)
+    got = d.fresh_workspace()
+    call = pkvg.prepare("gather_maybe_dequant_noalloc", d.src_cache(), got[: d.num_tokens, : d.entry],
+                        d.block_table, d.cu_seq_lens, d.num_reqs, "fp8", scale=d.scale_tensor,
+                        seq_starts=d.seq_starts)
+    for rep in range(2):
+        got.view(torch.uint8).fill_(workloads.SENTINEL_BYTE)
+        call()
+        ows = o.fresh_workspace()
+        pkvg.gather_maybe_dequant_noalloc(o.src_cache(), ows[: o.num_tokens, : o.entry], o.block_table,
+                                          o.cu_seq_lens, o.num_reqs, "auto", None, o.seq_starts)
+        torch.cuda.synchronize()
+        log(f"[noalloc] prepared call, issue {rep + 1}: R={d.num_reqs} T={d.num_tokens}")
+        assert torch.equal(want.view(torch.uint8).cpu(), got.view(torch.uint8).cpu()), rep
+
+
 def test_noalloc_full_size_named_workload():
     """A named workload at full size through both entry points (fused path)."""
     wl = workloads.named("mixed_fp8_dequant_strided")
