@@ -4,6 +4,8 @@ size, seeded random cases with every mask (padding rows, batch ids past the
 batch count, rows outside their batch, narrowed tables, out-of-range blocks),
 both record layouts, three head dimensions, 16-byte and byte-wise destination
 rows, and block addresses past 2^31 bytes."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -96,6 +98,32 @@ def test_indexer_random_small(seed):
             value_cols=hd + int(rng.choice([0, 0, 1, 3, 16])),   # odd pitches: byte path
             scale_cols=int(rng.choice([1, 2, 3])), allow_alias=bool(rng.random() < 0.3))
         check_indexer_parity(corrupt(iw, rng))
+
+
+def with_leading_rows(iw, lead: int, claim_first: bool):
+    """``iw`` behind ``lead`` rows that belong to no batch: every batch extent
+    moves down by ``lead`` (so cu_seqlen[0] == lead), and the new rows carry
+    batch id -1, or 0 with ``claim_first`` (outside batch 0's extent, masked)."""
+    sent = workloads.SENTINEL_BYTE
+    head = torch.full((lead,), 0 if claim_first else -1, dtype=torch.int32)
+    values = torch.cat([torch.full((lead, iw.values.shape[1]), sent, dtype=torch.uint8), iw.values])
+    scales = torch.cat([torch.full((lead, iw.scales.shape[1] * 4), sent, dtype=torch.uint8).view(torch.float32),
+                        iw.scales])
+    return dataclasses.replace(iw, name=f"{iw.name}_lead{lead}", token_to_seq=torch.cat([head, iw.token_to_seq]),
+                               cu_seqlen=iw.cu_seqlen + lead, num_tokens=iw.num_tokens + lead, values=values,
+                               scales=scales)
+
+
+@pytest.mark.parametrize("lead,claim_first", [(1, False), (63, True), (64, False), (100, True), (4097, False)])
+@pytest.mark.parametrize("layout", [workloads.INDEXER_LAYOUT_FLAT, workloads.INDEXER_LAYOUT_TILED])
+def test_indexer_first_batch_after_leading_rows(lead, claim_first, layout):
+    """A first batch that starts after row 0 (cu_seqlen[0] > 0): row r of batch 0
+    then lies at position r - cu_seqlen[0], not r, so the table column the kernel
+    requests ahead for first-batch rows (r / block_size) is theirs only where the
+    two columns coincide; every row must still take its own block."""
+    iw = workloads.make_indexer_workload(f"ix_lead_{layout}", [5000, 700, 0, 300], 64, 128, 120,
+                                         seed=4300 + lead, layout=layout, pad_rows=9)
+    check_indexer_parity(with_leading_rows(iw, lead, claim_first))
 
 
 @pytest.mark.parametrize("layout", [workloads.INDEXER_LAYOUT_FLAT, workloads.INDEXER_LAYOUT_TILED])
