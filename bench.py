@@ -19,7 +19,7 @@ synchronisation latencies and the spin.  The timed steps rotate over several cop
 inputs and outputs whose total is far above the 256 MB Infinity Cache, so no
 step finds its data in a cache.  Each workload also reports one cold call's
 latency (median, p10, p90 of 100: a 1 GiB fill or read, then events around one
-call) and the GB/s at that median; a single call from an idle GPU carries the
+call) and the GB/s at that median; a single call timed on its own carries the
 launch's own fixed cost (an empty kernel takes about 6 us that way).  Printed
 on stdout: ONE JSON line.  Progress goes to stderr.
 
@@ -433,8 +433,8 @@ def measure(wl, dev, args) -> dict:
         "config": workload_config(wl, alg_bytes),
         "pct_of_peak": round(100.0 * achieved / PEAK_HBM_GBS, 2),
         "median_latency_us_cold_scrubbed": round(cold["median_us"], 3),
-        # the same algorithmic bytes over the cold single call's median (one launch from an idle
-        # GPU, timed alone: it carries the launch's own fixed cost)
+        # the same algorithmic bytes over the cold single call's median (one launch timed on
+        # its own: it carries the launch's own fixed cost)
         "cold_single_call_gbs": round(alg_bytes / (cold["median_us"] * 1e-6) / 1e9, 2),
         "cold_single_call_pct_of_peak": round(100.0 * alg_bytes / (cold["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
         "per_launch_us": round(kern_ms * 1e3, 3),
