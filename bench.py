@@ -4,9 +4,11 @@ One step = one call of the library on one batch (all of the hot path: page-task
 build, block lookup, page copy / dequant), inputs already resident in HBM.
 Headline workload: one request of 307,200 tokens (4,800 pages of 64), 576 fp8
 e4m3fn codes per token upconverted to bf16 with a per-tensor scale, shuffled
-physical blocks.  The same run also times the second single-request gather
-(61,440 bf16 tokens, raw copy) with the same steps and warmup and reports it
-as a nested object.  Metric: effective HBM GB/s (algorithmic bytes read +
+physical blocks.  The same run also times, with the same steps and warmup,
+the second single-request gather (61,440 bf16 tokens, raw copy) and the
+indexer quant-cache gather (307,200 rows of 128 value bytes and a 4-byte
+scale, flat records), each reported as a nested object under its workload
+name.  Metric: effective HBM GB/s (algorithmic bytes read +
 written per step / time per step).
 
 Timing: exactly K back-to-back calls bracketed by torch.cuda.synchronize(),
@@ -23,7 +25,7 @@ call) and the GB/s at that median; a single call timed on its own carries the
 launch's own fixed cost (an empty kernel takes about 6 us that way).  Printed
 on stdout: ONE JSON line.  Progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also NAME,NAME]
 """
 from __future__ import annotations
 
@@ -43,7 +45,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
 SPACER_CYCLES = 200_000  # GPU clock cycles of the spin before the timed calls (tens of us)
 METRIC = "effective HBM GB/s (read+write) and % of peak; median gather latency, 1 GPU"
 DEFAULT_WORKLOAD = "single_300k_fp8_upconvert"
-SECOND_WORKLOAD = "single_60k_raw"
+ALSO_WORKLOADS = ("single_60k_raw", "indexer_single_300k_flat")
 TRAFFIC_DIR = os.path.join(REPO, "profiles")
 KERNEL_SOURCES = ["paged_kv_cache_device_amd/csrc/gather_kernels.hpp",
                   "paged_kv_cache_device_amd/csrc/indexer_kernels.hpp",
@@ -493,9 +495,9 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--also", default=SECOND_WORKLOAD,
-                    help="a second named workload timed in the same run and reported as a "
-                         "nested object ('' for none)")
+    ap.add_argument("--also", default=",".join(ALSO_WORKLOADS),
+                    help="comma-separated named workloads timed in the same run, each reported "
+                         "as a nested object under its name ('' for none)")
     ap.add_argument("--only-gather", action="store_true",
                     help="run warmup + steps of the gather and nothing else (for profilers)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -566,10 +568,12 @@ def main():
                         else wl.gathered_rows() * wl.entry * wl.dst_elem_bytes)
     copy_ref = copy_reference(payload_each_way, dev, args.steps, 3 << 30)
     log(f"[bench] device copy reference {copy_ref['gbs']:.0f} GB/s")
-    also = None
-    if args.also and args.also != wl.name and not args.lens:
-        log(f"[bench] second workload {args.also}: generating")
-        also = measure(workloads.named(args.also), dev, args)
+    also = []
+    for name in [a for a in args.also.split(",") if a] if not args.lens else []:
+        if name == wl.name:
+            continue
+        log(f"[bench] further workload {name}: generating")
+        also.append(measure(workloads.named(name), dev, args))
         torch.cuda.empty_cache()
 
     result = {
@@ -602,8 +606,8 @@ def main():
                                                          "maybe_dequant": "1.39-1.77"},
                     "pages_dram_fraction_of_peak": "0.75-0.84"},
     }
-    if also is not None:
-        result[also["config"]["workload"]] = also
+    for a in also:
+        result[a["config"]["workload"]] = a
     if not args.no_cpu:
         n = host_threads()
         log(f"[bench] timing the CPU oracle: {n} threads, then one (about 8 s each)")

@@ -170,13 +170,14 @@ def test_pages_uneven_test_shape(use_starts):
     assert u8.cache_base.dtype == torch.uint8 and u8.workspace.dtype == torch.uint8
 
 
-def test_bench_defaults_name_both_single_request_gathers():
+def test_bench_defaults_name_the_single_request_gathers_and_the_indexer():
     sys.path.insert(0, REPO)
     import bench
 
     assert bench.DEFAULT_WORKLOAD == "single_300k_fp8_upconvert"
-    assert bench.SECOND_WORKLOAD == "single_60k_raw"
-    assert set(workloads.NAMED) >= {bench.DEFAULT_WORKLOAD, bench.SECOND_WORKLOAD}
+    assert bench.ALSO_WORKLOADS == ("single_60k_raw", "indexer_single_300k_flat")
+    assert set(workloads.NAMED) >= {bench.DEFAULT_WORKLOAD, bench.ALSO_WORKLOADS[0]}
+    assert bench.ALSO_WORKLOADS[1] in workloads.INDEXER_NAMED
 
 
 @pytest.mark.parametrize("name,parts", [("indexer_tiny_flat", 4), ("indexer_skew8_tiled", 16)])
