@@ -63,19 +63,23 @@ struct IndexerParams {
   uint32_t scale_area;            // block_size * HEAD_DIM: byte of the first scale in a record
 };
 
-constexpr int kIndexerThreads = 256;
+// One wave per workgroup: the dispatcher then spreads the waves evenly over
+// the CUs, where workgroups of four waves left some CUs a third more rows than
+// others (single sequences of 76,800 rows 6.5 -> 5.8 us, skew-8 10.3 -> 9.5
+// us, 300K rows 16.1 -> 16.0 us; 128-thread workgroups in between, 512 and
+// 1024 slower still).
+constexpr int kIndexerThreads = 64;
 constexpr int kIndexerRowsPerWave = 64;
 
-// Where a row's batch extent cu_seqlen[b], cu_seqlen[b + 1] comes from.  The
-// array is loaded together with token_to_seq (one round trip) when it is small
-// enough, instead of after it (a second dependent round trip):
+// Where a row's batch extent cu_seqlen[b], cu_seqlen[b + 1] comes from.  When
+// the array fits in a wave's lanes it is loaded together with token_to_seq
+// (one round trip); larger ones are read per row after its batch id (a second
+// round trip, but measured faster than copying the array into LDS first:
+// 64 to 4,095 batches over 300,000 rows 16.6-17.1 -> 15.8-16.2 us).
 enum IndexerCuSource : int {
   kCuWave = 0,    // num_batches + 1 <= 64: lane i of every wave holds cu_seqlen[i]
-  kCuLds = 1,     // num_batches + 1 <= kIndexerLdsCuMax: the workgroup copies it into LDS
-  kCuGlobal = 2,  // larger: each row loads its two entries after its batch id
+  kCuGlobal = 1,  // larger: each row loads its two entries after its batch id
 };
-constexpr int kIndexerLdsCuMax = 4096;
-static_assert(kIndexerLdsCuMax % kIndexerThreads == 0, "whole rounds of a workgroup's loads");
 
 // Byte offset of chunk j (bytes j*W .. j*W+W-1 of a token) from the token's
 // first value byte (indexer_row_base): consecutive in the flat layout; in the
@@ -123,8 +127,8 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
 // a single call leaves nothing dirty in L2 for its end to write back (the
 // 300K flat gather's cold call 19.2 -> 18.7 us; back to back unchanged).
 
-// Grid: any size; wave w of workgroup g takes rows from (g * 4 + w) * 64 on,
-// striding by the grid's rows.  Source rows are dword-aligned (the host checks
+// Grid: any size; wave w of workgroup g takes rows from (g * WAVES + w) * 64
+// on, striding by the grid's rows.  Source rows are dword-aligned (the host checks
 // the cache base and the record stride; value rows start at multiples of 16
 // bytes inside a record), so bit 0 of a row's offset carries its mask when
 // the offset crosses lanes.  The host launches only with num_tokens,
@@ -133,7 +137,7 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
 // speculative table entry lies in row 0 below the width, so every load is in
 // bounds and goes out without a branch, and only the stores are masked.  W == 16 needs dword-aligned
 // destination rows and 64 * dst_value_stride < 2^31 (the host picks W == 1
-// otherwise).  Dynamic LDS (kCuLds): (num_batches + 1) int32.
+// otherwise).  No LDS.
 //
 // The fields the first two dependent loads need (batch ids, batch extents,
 // their counts, the block table and its geometry) are leading scalar
@@ -166,7 +170,6 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(
   constexpr int PER_LANE = CPR;
   constexpr int BATCH = PER_LANE < 16 ? PER_LANE : 16;
   static_assert(PER_LANE % BATCH == 0, "whole batches");
-  extern __shared__ int32_t cu_lds[];
   const int lane = threadIdx.x & 63;
   // wave-uniform, so a wave's row range and its destination resource sit in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -176,30 +179,11 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(
   // The first rows' batch ids and the batch extents leave first thing, from
   // preloaded arguments only: the loop below needs fields of the parameter
   // struct, and the compiler waits for their scalar loads before its body.
-  // Every wave gets here (a wave past the last row reads row num_tokens - 1
-  // and skips the loop), so all of a workgroup's waves reach the barrier.
+  // (A wave past the last row reads row num_tokens - 1 and skips the loop.)
   const int32_t first_row = static_cast<int32_t>(first_row0) + lane;
   const int32_t first_batch = p.token_to_seq[first_row < p.num_tokens ? first_row : p.num_tokens - 1];
   int32_t cu_lane = 0;
-  if constexpr (CU == kCuWave) {
-    cu_lane = p.cu_seqlen[lane < ncu ? lane : ncu - 1];
-  } else if constexpr (CU == kCuLds) {
-    // at most 16 entries per thread, all requested before any is written (a
-    // load-then-store loop would wait for each in turn)
-    constexpr int kPer = kIndexerLdsCuMax / kIndexerThreads;
-    int32_t e[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = static_cast<int>(threadIdx.x) + k * kIndexerThreads;
-      e[k] = p.cu_seqlen[i < ncu ? i : ncu - 1];
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = static_cast<int>(threadIdx.x) + k * kIndexerThreads;
-      if (i < ncu) cu_lds[i] = e[k];
-    }
-    __syncthreads();
-  }
+  if constexpr (CU == kCuWave) cu_lane = p.cu_seqlen[lane < ncu ? lane : ncu - 1];
   // A speculative block-table entry, requested with the batch ids: row 0's
   // column first_row / block_size, the column of a row of batch 0 when
   // cu_seqlen[0] == 0.  A first-round row whose batch turns out to be 0 and
@@ -222,9 +206,6 @@ __global__ __launch_bounds__(kIndexerThreads) void indexer_gather_kernel(
     if constexpr (CU == kCuWave) {
       start = __shfl(cu_lane, b, 64);
       end = __shfl(cu_lane, b + 1, 64);
-    } else if constexpr (CU == kCuLds) {
-      start = cu_lds[b];
-      end = cu_lds[b + 1];
     } else {
       start = p.cu_seqlen[b];
       end = p.cu_seqlen[b + 1];

@@ -665,12 +665,9 @@ bool indexer_structure_supported(int32_t layout, int32_t head_dim, int32_t block
 template <int LAYOUT, int HEAD_DIM, int BT, int HT, int W>
 hipError_t launch_indexer_cu(const pkvg::IndexerParams& p, unsigned grid, hipStream_t stream) {
   const int32_t ncu = p.num_batches + 1;
-  const int cu = ncu <= 64 ? pkvg::kCuWave : (ncu <= pkvg::kIndexerLdsCuMax ? pkvg::kCuLds : pkvg::kCuGlobal);
-  const size_t lds = cu == pkvg::kCuLds ? sizeof(int32_t) * size_t(ncu) : 0;
-  auto kernel = cu == pkvg::kCuWave  ? pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuWave>
-                : cu == pkvg::kCuLds ? pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuLds>
-                                     : pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuGlobal>;
-  return launch(kernel, grid, pkvg::kIndexerThreads, lds, stream, p.token_to_seq, p.cu_seqlen, p.num_tokens,
+  auto kernel = ncu <= 64 ? pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuWave>
+                          : pkvg::indexer_gather_kernel<LAYOUT, HEAD_DIM, BT, HT, W, pkvg::kCuGlobal>;
+  return launch(kernel, grid, pkvg::kIndexerThreads, 0, stream, p.token_to_seq, p.cu_seqlen, p.num_tokens,
                 p.num_batches, p.block_table, p.block_table_ld, p.block_table_width, p.block_size,
                 p.block_size_magic, p);
 }
@@ -691,10 +688,10 @@ hipError_t launch_indexer_dim(const pkvg::IndexerParams& p, int32_t head_dim, bo
   }
 }
 
-// Rows per workgroup (four waves of 64 rows); the grid covers every row once,
-// up to this many workgroups (8 times what the chip holds at once; more rows,
-// past 4,194,304, are taken by striding).
-constexpr int64_t kIndexerMaxGrid = int64_t(1) << 14;
+// Rows per workgroup (one wave of 64 rows); the grid covers every row once,
+// up to this many workgroups (far more than the chip holds at once; more
+// rows, past 4,194,304, are taken by striding).
+constexpr int64_t kIndexerMaxGrid = int64_t(1) << 16;
 
 // Validates an indexer gather and fills its parameters; touches no device.
 int prepare_indexer(const void* cache, int64_t num_blocks, int32_t block_size, int64_t block_stride,

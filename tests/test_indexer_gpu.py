@@ -207,9 +207,9 @@ def test_indexer_block_addresses_beyond_2_to_31():
 
 @pytest.mark.parametrize("B", [63, 64, 100, 4095, 4096, 6000])
 def test_indexer_many_batches(B):
-    """Batch extents from wave registers (up to 63 batches), LDS (up to 4,095)
-    and global loads (more): both sides of each switch, with rows claiming
-    other batches and padding rows."""
+    """Batch extents from wave registers (up to 63 batches) and from per-row
+    loads (more): both sides of the switch and batch counts far past it, with
+    rows claiming other batches and padding rows."""
     rng = np.random.default_rng(B)
     lens = rng.integers(0, 40, size=B).tolist()
     pages = sum(-(-n // 16) for n in lens)
@@ -286,12 +286,12 @@ def test_indexer_destination_pitch_at_the_store_range(pitch):
 
 
 def test_indexer_rows_beyond_the_grid():
-    """More rows than one pass of the capped grid covers (16,384 workgroups of
-    256 rows = 4,194,304 rows): waves stride to their next 64 rows and load
+    """More rows than one pass of the capped grid covers (65,536 workgroups of
+    64 rows = 4,194,304 rows): waves stride to their next 64 rows and load
     those rows' batch ids inside the loop.  One sequence of 4,300,000 tokens
     and padding rows past it."""
     n = 4_300_000
     iw = workloads.make_indexer_workload("ix_grid_cap", [n], 64, 128, -(-n // 64) + 5, seed=81,
                                          pad_rows=70)
-    assert iw.num_tokens > 16384 * 256
+    assert iw.num_tokens > 65536 * 64
     check_indexer_parity(iw)
