@@ -22,7 +22,7 @@
 //
 // Design for gfx950: the work unit is the output row (token_to_seq may send
 // any row to any batch, and padding rows carry -1), so a wave owns 64
-// consecutive rows.  Lane r resolves row r (token_to_seq, the batch's extent,
+// consecutive rows, and is a workgroup of its own.  Lane r resolves row r (token_to_seq, the batch's extent,
 // the block-table entry: dependent loads, the entry of a row of the first
 // batch requested ahead, speculatively) to a source address; then
 // the wave moves the 64 rows' value bytes in W-byte chunks, consecutive lanes
@@ -128,16 +128,16 @@ __device__ __forceinline__ V load_cache(IndexerCache base, uint64_t off) {
 // 300K flat gather's cold call 19.2 -> 18.7 us; back to back unchanged).
 
 // Grid: any size; wave w of workgroup g takes rows from (g * WAVES + w) * 64
-// on, striding by the grid's rows.  Source rows are dword-aligned (the host checks
-// the cache base and the record stride; value rows start at multiples of 16
-// bytes inside a record), so bit 0 of a row's offset carries its mask when
-// the offset crosses lanes.  The host launches only with num_tokens,
+// on, striding by the grid's rows.  Source rows are dword-aligned (the host
+// checks the cache base and the record stride; value rows start at multiples
+// of 16 bytes inside a record), so bit 0 of a row's offset carries its mask
+// when the offset crosses lanes.  The host launches only with num_tokens,
 // num_batches, num_blocks and block_table_width all >= 1 (otherwise every row
 // is masked): a masked row keeps an offset inside record 0, and the
 // speculative table entry lies in row 0 below the width, so every load is in
-// bounds and goes out without a branch, and only the stores are masked.  W == 16 needs dword-aligned
-// destination rows and 64 * dst_value_stride < 2^31 (the host picks W == 1
-// otherwise).  No LDS.
+// bounds and goes out without a branch, and only the stores are masked.
+// W == 16 needs dword-aligned destination rows and 64 * dst_value_stride <
+// 2^31 (the host picks W == 1 otherwise).  No LDS.
 //
 // The fields the first two dependent loads need (batch ids, batch extents,
 // their counts, the block table and its geometry) are leading scalar
